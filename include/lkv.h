@@ -1,0 +1,275 @@
+/*
+ * lkv.h -- C ABI of liblkv: decode attention over a compressed (latent) KV
+ * cache on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes is stated by the pages it is built from:
+ *   [GQLA] "GQLA: Group-Query Latent Attention for Hardware-Adaptive Large
+ *          Language Model Decoding" (gist.science explainer), technical
+ *          summary section 2 "Methodology": the MQA-absorbed path (all h_q
+ *          query heads, W_UK folded into the query, attend over one shared
+ *          per-token latent c_KV of width r_kv = d_c plus one shared RoPE key
+ *          of width d^R_h = d_rope; the latent is also the value, and the
+ *          output P.c_KV goes on to the folded W_UV), and the GQA path (the
+ *          latent expanded once into g key/value groups of width d_h, stored
+ *          beside the shared RoPE key; decode then runs plain grouped-query
+ *          attention with no per-step expansion); W_UK and W_UV indexed by
+ *          group.
+ *   [GLA]  article on Grouped-Tied / Grouped Latent Attention (Zadouri,
+ *          Strauss, Dao), section on GLA: a few latent heads, each shared by
+ *          a group of query heads.
+ *   [X]    X post by @classiclarryd on MLA vs GQA: GQA "copies" one KV head
+ *          per group of query heads.
+ * Paging, per-sequence lengths, the LSE output and split-KV are the
+ * serving-side statement of the same problem; the pages do not fix them, and
+ * this header does.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer named "device" is a HIP device pointer on the current
+ *    device; "host" pointers are ordinary host memory.  The caller allocates
+ *    and owns every buffer, workspace included.  The library keeps no pointer
+ *    after a call returns and never allocates device memory.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Buffers must stay alive until that stream work completes.
+ *  - Every argument struct begins with `struct_size`, which must equal
+ *    sizeof(the struct) as compiled against this header.
+ *  - Strides are in elements.  Query, output and LSE arrays are dense,
+ *    row-major, in the shapes given.
+ *  - Cache tokens: the block table (device, int32 [batch, max_pages]) maps
+ *    logical token j of sequence b to physical page block_table[b][j /
+ *    page_size], slot j % page_size.  Entries past a sequence's last page are
+ *    never read (padding such as -1 is fine).  Slots past the sequence length
+ *    are never read either: they may hold any bits, NaN included.
+ *  - seqlens (device, int32 [batch]) is the total cache length L_b,
+ *    including the s_q tokens of this step, which already sit at positions
+ *    L_b - s_q .. L_b - 1.  With causal != 0, query token t sees cache
+ *    positions [0, L_b - s_q + t]; with causal == 0 it sees [0, L_b).  A row
+ *    that sees no token (L_b == 0, or L_b < s_q when causal) yields O = 0 and
+ *    LSE = -inf.  Device-resident values (lengths, table entries) are a
+ *    caller contract: 0 <= L_b <= max_pages * page_size and every table entry
+ *    of a used page names a page inside the cache.
+ *  - Scores are softmax_scale * <q, k>; LSE is the natural log of the sum of
+ *    exp(score) over the visible tokens, in float32.
+ *  - Outputs have the input dtype; bf16 paths round to nearest even.  bf16
+ *    inputs are multiplied on the MFMA units with float32 accumulation; the
+ *    softmax probabilities are rounded to bf16 before the P.V product.
+ *  - Errors: every host-checkable precondition is checked before any launch;
+ *    a failure returns a status other than LKV_OK, launches nothing and
+ *    leaves a message readable through lkv_last_error() on the calling
+ *    thread.  No exception and no abort crosses this boundary.
+ */
+#ifndef LKV_H
+#define LKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LKV_ABI_VERSION 1
+
+typedef enum {
+  LKV_OK = 0,
+  LKV_ERR_NULL = 1,        /* a required pointer is NULL */
+  LKV_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  LKV_ERR_UNSUPPORTED = 3, /* no kernel for this dtype / width / page size */
+  LKV_ERR_ALIGN = 4,       /* a pointer or stride breaks the 16-byte rule */
+  LKV_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+  LKV_ERR_HIP = 6,         /* a HIP runtime call failed (message has details) */
+  LKV_ERR_STRUCT = 7       /* struct_size does not match this header */
+} lkv_status;
+
+typedef enum { LKV_F32 = 0, LKV_BF16 = 1 } lkv_dtype;
+
+/* LKV_ABI_VERSION of the built library. */
+int lkv_abi_version(void);
+
+/* Text of the last non-OK status returned on the calling thread ("" if
+ * none).  The pointer stays valid until the next call on that thread. */
+const char *lkv_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * lkv_mla_decode -- MLA absorbed decode [GQLA section 2, MQA-absorbed path;
+ * GLA section for n_latent > 1].
+ *
+ * For row (b, t, h), latent head l = h / (h_q / n_latent):
+ *   score_j = softmax_scale * ( <q_nope[b,t,h,:], c_kv(j, l)>
+ *                             + <q_rope[b,t,h,:], k_rope(j)> )
+ *   out[b,t,h,:] = sum_j softmax(score)_j * c_kv(j, l)      (latent = value)
+ *   lse[b,t,h]   = ln sum_j exp(score_j)
+ *
+ *   q_nope  device [batch, s_q, h_q, d_c]      absorbed query (W_UK folded in)
+ *   q_rope  device [batch, s_q, h_q, d_rope]
+ *   c_kv    device, element (page p, slot s, latent l, d) at
+ *           (p*page_size + s)*kv_tok_stride + l*d_c + d
+ *   k_rope  device, element (p, s, e) at (p*page_size + s)*rope_tok_stride + e
+ *           (one RoPE key shared by every latent head).  c_kv and k_rope may
+ *           alias one packed [.., n_latent*d_c + d_rope] buffer.
+ *   out     device [batch, s_q, h_q, d_c], dtype of the inputs
+ *   lse     device float32 [batch, s_q, h_q], or NULL
+ *   workspace  device, at least lkv_mla_decode_workspace_size() bytes, 256-byte
+ *           aligned.  Its contents need no initialisation and are scratch.
+ *   num_splits  0 = automatic.  Otherwise the number of equal shares the
+ *           concatenated cache tiles of the batch are cut into per query-row
+ *           group (split-KV; a share may span several sequences and a
+ *           sequence several shares; partial results are merged with the
+ *           LSE-weighted combine of lkv_split_combine).
+ *   seqlens_host  host int32 [batch] copy of seqlens, or NULL.  Used only to
+ *           skip the combine pass when no sequence is split; it must then
+ *           equal the device values.
+ * Supported: bf16 with d_c in {64, 128, 256, 512}, d_rope in {0, 16, 32, 64},
+ *   (h_q / n_latent) * s_q a multiple of 16 or at most 16... see
+ *   LKV_ERR_UNSUPPORTED text; f32 with d_c + d_rope <= 1024.  Any page_size
+ *   >= 1.  Pointers 16-byte aligned, strides multiples of 8 elements (bf16)
+ *   or 4 (f32).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  uint32_t struct_size;
+  int32_t dtype; /* lkv_dtype */
+  int32_t batch, s_q, h_q, n_latent, d_c, d_rope, page_size, max_pages;
+  float softmax_scale;
+  int32_t causal;
+  int32_t num_splits;
+  const void *q_nope;
+  const void *q_rope;
+  const void *c_kv;
+  int64_t kv_tok_stride;
+  const void *k_rope;
+  int64_t rope_tok_stride;
+  const int32_t *block_table;
+  const int32_t *seqlens;
+  const int32_t *seqlens_host;
+  void *out;
+  float *lse;
+  void *workspace;
+  size_t workspace_bytes;
+  void *stream; /* hipStream_t */
+} lkv_mla_args;
+
+lkv_status lkv_mla_decode(const lkv_mla_args *args);
+
+/* Workspace bytes lkv_mla_decode needs for these arguments (pointers may be
+ * NULL; only sizes, dtype and num_splits are read). */
+lkv_status lkv_mla_decode_workspace_size(const lkv_mla_args *args, size_t *bytes);
+
+/* ------------------------------------------------------------------------
+ * lkv_gqa_decode -- grouped-query decode over an expanded cache [GQLA
+ * section 2, GQA path: g groups of K/V width d_h plus the shared RoPE key;
+ * with d_rope == 0 it is plain GQA, the X post's "copying"].
+ *
+ * For row (b, t, h), KV head g = h / (h_q / n_kv):
+ *   score_j = softmax_scale * ( <q[b,t,h,:], K(j, g)> + <q_rope[b,t,h,:], k_rope(j)> )
+ *   out[b,t,h,:] = sum_j softmax(score)_j * V(j, g)
+ *
+ *   q        device [batch, s_q, h_q, d_h]
+ *   q_rope   device [batch, s_q, h_q, d_rope], NULL iff d_rope == 0
+ *   k_cache  device, element (p, s, g, d) at (p*page_size + s)*k_tok_stride + g*d_h + d
+ *   v_cache  device, element (p, s, g, d) at (p*page_size + s)*v_tok_stride + g*d_h + d
+ *   k_rope   device, as in lkv_mla_args; NULL iff d_rope == 0
+ *   out      device [batch, s_q, h_q, d_h];  lse device float32 [batch, s_q, h_q] or NULL
+ *   workspace / num_splits / seqlens_host as in lkv_mla_args.
+ * Supported: bf16 with d_h in {64, 128, 256}, d_rope in {0, 16, 32, 64}; f32
+ *   with d_h + d_rope <= 1024.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  uint32_t struct_size;
+  int32_t dtype;
+  int32_t batch, s_q, h_q, n_kv, d_h, d_rope, page_size, max_pages;
+  float softmax_scale;
+  int32_t causal;
+  int32_t num_splits;
+  const void *q;
+  const void *q_rope;
+  const void *k_cache;
+  int64_t k_tok_stride;
+  const void *v_cache;
+  int64_t v_tok_stride;
+  const void *k_rope;
+  int64_t rope_tok_stride;
+  const int32_t *block_table;
+  const int32_t *seqlens;
+  const int32_t *seqlens_host;
+  void *out;
+  float *lse;
+  void *workspace;
+  size_t workspace_bytes;
+  void *stream;
+} lkv_gqa_args;
+
+lkv_status lkv_gqa_decode(const lkv_gqa_args *args);
+lkv_status lkv_gqa_decode_workspace_size(const lkv_gqa_args *args, size_t *bytes);
+
+/* ------------------------------------------------------------------------
+ * lkv_gqla_expand_latent -- cache-write-time expansion of the latent into g
+ * key/value groups [GQLA section 2, GQA path: expanded once, then no
+ * per-step latent expansion].
+ *
+ * For every sequence b and token j in [start_pos[b], seqlens[b]), with
+ * row = block_table[b][j / page_size]*page_size + j % page_size:
+ *   k_out(row, g, :) = c_kv(row, :) . W_UK[g]      (d_c -> d_h)
+ *   v_out(row, g, :) = c_kv(row, :) . W_UV[g]
+ * computed with float32 accumulation and rounded to bf16 (nearest even).
+ * The expanded caches use the same page ids as the latent cache.
+ *
+ *   c_kv    device bf16, element (row, d) at row*kv_tok_stride + d
+ *   w_uk, w_uv  device bf16 [g, d_c, d_h] (row-major: d_c rows of d_h)
+ *   start_pos   device int32 [batch] or NULL (= 0): append-only expansion
+ *   k_out, v_out  device bf16, element (row, g, e) at row*k_tok_stride + g*d_h + e
+ *                 (v_tok_stride for v_out)
+ * Supported: bf16, d_c a multiple of 64 up to 1024, d_h in {64, 128, 256}.
+ * Rows outside [start_pos, seqlens) are not written.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  uint32_t struct_size;
+  int32_t dtype;
+  int32_t batch, g, d_c, d_h, page_size, max_pages;
+  const void *c_kv;
+  int64_t kv_tok_stride;
+  const void *w_uk;
+  const void *w_uv;
+  const int32_t *block_table;
+  const int32_t *seqlens;
+  const int32_t *start_pos;
+  void *k_out;
+  int64_t k_tok_stride;
+  void *v_out;
+  int64_t v_tok_stride;
+  void *stream;
+} lkv_expand_args;
+
+lkv_status lkv_gqla_expand_latent(const lkv_expand_args *args);
+
+/* ------------------------------------------------------------------------
+ * lkv_split_combine -- merge split-KV partial results with their LSEs.
+ * For sequence b, works w in [work_offsets[b], work_offsets[b+1]):
+ *   lse = ln sum_w exp(lse_part[w]),  out = sum_w exp(lse_part[w] - lse) o_part[w]
+ * A work with lse_part = -inf contributes nothing; a sequence with no
+ * contributing work gets out = 0 and lse = -inf.
+ *
+ *   o_part        device float32 [n_work, s_q, h_q, d_v]
+ *   lse_part      device float32 [n_work, s_q, h_q]
+ *   work_offsets  device int32 [batch + 1], non-decreasing, last = n_work
+ *   out           device [batch, s_q, h_q, d_v] of `dtype`; lse float32 or NULL
+ * Supported: d_v a multiple of 4 up to 1024.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  uint32_t struct_size;
+  int32_t dtype;
+  int32_t batch, s_q, h_q, d_v, n_work;
+  const float *o_part;
+  const float *lse_part;
+  const int32_t *work_offsets;
+  void *out;
+  float *lse;
+  void *stream;
+} lkv_combine_args;
+
+lkv_status lkv_split_combine(const lkv_combine_args *args);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LKV_H */

@@ -1,0 +1,75 @@
+// lkv_internal.h -- parameter blocks and launcher declarations shared by the
+// C ABI (abi.cpp) and the HIP kernel files.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lkv {
+
+// Cache tokens per tile: the unit of work of the decode kernels and of the
+// split-KV planner.
+constexpr int kTile = 64;
+
+// One decode pass, latent (MLA) or expanded (GQA) cache.  "KV head" below is
+// the latent head of the MLA path or the KV group of the GQA path; query head
+// h uses KV head h / hpk.
+struct DecodeParams {
+  const void *q;       // [B, s_q, h_q, dk]
+  const void *q_rope;  // [B, s_q, h_q, dr] (dr > 0)
+  const void *k;       // key main part: token row r, KV head g at r*k_stride + g*dk
+  const void *r;       // shared RoPE key: token row r at r*r_stride
+  const void *v;       // value: token row r, KV head g at r*v_stride + g*dv
+  long long k_stride, r_stride, v_stride;
+  const int32_t *block_table;  // [B, max_pages]
+  const int32_t *seqlens;      // [B]
+  void *out;                   // [B, s_q, h_q, dv]
+  float *lse;                  // [B, s_q, h_q] or null
+  float *o_part;               // [slots, s_q, h_q, dv]
+  float *lse_part;             // [slots, s_q, h_q]
+  int32_t *meta;               // [B][2]: first partial slot, number of partials
+  int B, s_q, h_q, n_kvh, hpk;
+  int page_size, page_shift;   // page_shift = log2(page_size) or -1
+  int max_pages;
+  int rows_per_kvh;            // s_q * hpk
+  int row_tiles;               // ceil(rows_per_kvh / ROWS)
+  int n_chunks;                // split-KV shares of the concatenated tiles
+  int causal;
+  float scale_log2;            // softmax scale * log2(e)
+  int dk, dr, dv;              // widths (used by the generic fp32 kernel)
+};
+
+struct CombineParams {
+  const float *o_part;
+  const float *lse_part;
+  const int32_t *meta;          // [B][2] (start, count) when offsets == null
+  const int32_t *offsets;       // [B+1] or null
+  void *out;
+  float *lse;
+  int B, s_q, h_q, dv;
+  int skip_single;              // 1: sequences with <= 1 partial are already final
+  int out_bf16;
+};
+
+struct ExpandParams {
+  const void *c;                // latent, row r at r*c_stride
+  long long c_stride;
+  const void *w_uk, *w_uv;      // [g, d_c, d_h]
+  const int32_t *block_table, *seqlens, *start_pos;
+  void *k_out, *v_out;
+  long long k_stride, v_stride;
+  int B, g, d_c, d_h, page_size, max_pages;
+};
+
+// Launchers return hipSuccess or the launch error.  `bf16_variant` selects a
+// compiled instantiation; launchers return hipErrorInvalidValue when none
+// matches (the ABI checks support before calling).
+bool mfma_decode_supported(int dk, int dr, int dv, bool v_alias, int rows_per_kvh);
+int mfma_decode_rows(int rows_per_kvh);  // ROWS template used for this problem
+hipError_t launch_mfma_decode(const DecodeParams &p, bool v_alias, int rows, hipStream_t s);
+hipError_t launch_f32_decode(const DecodeParams &p, hipStream_t s);
+hipError_t launch_combine(const CombineParams &p, hipStream_t s);
+bool expand_supported(int d_c, int d_h);
+hipError_t launch_expand(const ExpandParams &p, hipStream_t s);
+
+}  // namespace lkv

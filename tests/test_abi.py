@@ -1,0 +1,199 @@
+"""C ABI contract tests that need no GPU: the library loads, exports every
+function include/lkv.h declares, its argument structs match the Python
+binding byte for byte, and host-checkable preconditions fail fast with the
+documented status (no launch, no device access)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import latent_kv_decode_amd as lkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lkv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return lkv.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert set(names) == set(lkv.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), f"{n} missing from liblkv.so"
+
+
+def test_abi_version(lib):
+    assert lkv.lkv_abi_version() == 1
+
+
+def _c_layout(struct, fields):
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"lkv.h\"\nint main(){\n"
+    src += f'printf("%zu\\n", sizeof({struct}));\n'
+    for f in fields:
+        src += f'printf("%zu\\n", offsetof({struct}, {f}));\n'
+    src += "return 0;}\n"
+    tmp = os.path.join(os.environ.get("TMPDIR", "/tmp"), f"lkv_layout_{struct}")
+    with open(tmp + ".c", "w") as fh:
+        fh.write(src)
+    subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), tmp + ".c", "-o", tmp])
+    vals = [int(v) for v in subprocess.check_output([tmp]).split()]
+    return vals[0], vals[1:]
+
+
+@pytest.mark.parametrize("py,c", [(lkv.MlaArgs, "lkv_mla_args"), (lkv.GqaArgs, "lkv_gqa_args"),
+                                  (lkv.ExpandArgs, "lkv_expand_args"),
+                                  (lkv.CombineArgs, "lkv_combine_args")])
+def test_struct_layouts_match_header(py, c):
+    fields = [f for f, _ in py._fields_]
+    size, offs = _c_layout(c, fields)
+    assert ctypes.sizeof(py) == size
+    for (f, _), off in zip(py._fields_, offs):
+        assert getattr(py, f).offset == off, f
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails validation first
+
+
+def _mla(**kw):
+    a = lkv.MlaArgs()
+    a.struct_size = ctypes.sizeof(lkv.MlaArgs)
+    a.dtype = lkv.LKV_BF16
+    a.batch, a.s_q, a.h_q, a.n_latent, a.d_c, a.d_rope = 2, 1, 128, 1, 512, 64
+    a.page_size, a.max_pages = 64, 4
+    a.softmax_scale = 0.04
+    a.causal = 1
+    for f in ("q_nope", "q_rope", "c_kv", "k_rope", "block_table", "seqlens", "out", "lse"):
+        setattr(a, f, FAKE)
+    a.workspace = FAKE
+    a.kv_tok_stride = 576
+    a.rope_tok_stride = 576
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _status(lib, a):
+    return lib.lkv_mla_decode(ctypes.byref(a))
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(struct_size=12), 7),
+    (dict(dtype=5), 3),
+    (dict(h_q=100, n_latent=3), 2),
+    (dict(d_c=320), 3),
+    (dict(d_rope=16), 3),
+    (dict(s_q=0), 2),
+    (dict(batch=-1), 2),
+    (dict(page_size=0), 2),
+    (dict(num_splits=-2), 2),
+    (dict(q_nope=None), 1),
+    (dict(seqlens=None), 1),
+    (dict(k_rope=None), 1),
+    (dict(out=FAKE + 2), 4),
+    (dict(kv_tok_stride=580), 4),
+    (dict(kv_tok_stride=256), 2),
+    (dict(workspace=None), 5),
+    (dict(workspace=FAKE + 16), 4),
+])
+def test_mla_validation(lib, change, expect):
+    st = _status(lib, _mla(**change))
+    assert st == expect, (st, lkv.lkv_last_error())
+    assert lkv.lkv_last_error() != ""
+
+
+def test_null_args(lib):
+    assert lib.lkv_mla_decode(None) == 1
+    assert lib.lkv_gqa_decode(None) == 1
+    assert lib.lkv_gqla_expand_latent(None) == 1
+    assert lib.lkv_split_combine(None) == 1
+
+
+def test_batch_zero_is_ok_without_pointers(lib):
+    a = _mla(batch=0, q_nope=None, c_kv=None, out=None)
+    assert _status(lib, a) == 0
+
+
+def _gqa(**kw):
+    a = lkv.GqaArgs()
+    a.struct_size = ctypes.sizeof(lkv.GqaArgs)
+    a.dtype = lkv.LKV_BF16
+    a.batch, a.s_q, a.h_q, a.n_kv, a.d_h, a.d_rope = 2, 1, 32, 8, 128, 0
+    a.page_size, a.max_pages = 64, 4
+    a.softmax_scale = 0.09
+    for f in ("q", "k_cache", "v_cache", "block_table", "seqlens", "out", "workspace"):
+        setattr(a, f, FAKE)
+    a.k_tok_stride = a.v_tok_stride = 1024
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(h_q=30), 2), (dict(d_h=96), 3), (dict(v_cache=None), 1), (dict(q_rope=FAKE), 2),
+    (dict(d_rope=64), 1), (dict(v_tok_stride=512), 2), (dict(k_tok_stride=1028), 4)])
+def test_gqa_validation(lib, change, expect):
+    st = lib.lkv_gqa_decode(ctypes.byref(_gqa(**change)))
+    assert st == expect, (st, lkv.lkv_last_error())
+
+
+def _expand(**kw):
+    a = lkv.ExpandArgs()
+    a.struct_size = ctypes.sizeof(lkv.ExpandArgs)
+    a.dtype = lkv.LKV_BF16
+    a.batch, a.g, a.d_c, a.d_h, a.page_size, a.max_pages = 2, 8, 512, 128, 64, 4
+    for f in ("c_kv", "w_uk", "w_uv", "block_table", "seqlens", "k_out", "v_out"):
+        setattr(a, f, FAKE)
+    a.kv_tok_stride, a.k_tok_stride, a.v_tok_stride = 576, 1024, 1024
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(dtype=0), 3), (dict(d_c=1024), 3), (dict(d_h=96), 3), (dict(w_uv=None), 1),
+    (dict(k_out=FAKE + 8), 4), (dict(kv_tok_stride=500), 4), (dict(k_tok_stride=512), 2),
+    (dict(g=0), 2), (dict(struct_size=3), 7)])
+def test_expand_validation(lib, change, expect):
+    st = lib.lkv_gqla_expand_latent(ctypes.byref(_expand(**change)))
+    assert st == expect, (st, lkv.lkv_last_error())
+
+
+def _combine(**kw):
+    a = lkv.CombineArgs()
+    a.struct_size = ctypes.sizeof(lkv.CombineArgs)
+    a.dtype = lkv.LKV_BF16
+    a.batch, a.s_q, a.h_q, a.d_v, a.n_work = 2, 1, 16, 512, 4
+    for f in ("o_part", "lse_part", "work_offsets", "out"):
+        setattr(a, f, FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(d_v=6), 3), (dict(d_v=2048), 3), (dict(o_part=None), 1), (dict(o_part=FAKE + 4), 4),
+    (dict(dtype=9), 3), (dict(s_q=0), 2)])
+def test_combine_validation(lib, change, expect):
+    st = lib.lkv_split_combine(ctypes.byref(_combine(**change)))
+    assert st == expect, (st, lkv.lkv_last_error())
+
+
+def test_binding_raises_when_library_missing(tmp_path):
+    with pytest.raises(ImportError):
+        lkv._lib_backup = lkv._lib
+        try:
+            lkv._lib = None
+            lkv.load_library(str(tmp_path / "nope.so"))
+        finally:
+            lkv._lib = lkv._lib_backup

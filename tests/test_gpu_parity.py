@@ -1,0 +1,430 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle on
+the same seeded inputs.
+
+Small cases span several 64-token tiles, ragged tails, NaN-poisoned unused
+slots and pages, both s_q readings (causal and not), several split plans and
+every compiled head width.  Full-size cases run the workloads at their real
+shapes in the launch configuration the benchmark times and compare sampled
+rows with the oracle computed row by row.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import lkv_inputs as li
+from tests.gpu_common import (assert_close, from_dev, mla_device_inputs, note, oracle_mla,
+                              rows_of, run_mla, small_mla, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def lkv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import latent_kv_decode_amd as m
+    m.load_library()
+    return m
+
+
+@pytest.fixture(scope="module")
+def oracle():
+    import oracle as o
+    o.build(force=False)
+    return o
+
+
+# ------------------------------------------------------------------ fp32 tiny
+def test_tiny_fp32_workload(lkv, oracle):
+    w = li.workload("tiny_mla_fp32")
+    x = li.generate(w)
+    note("case tiny_mla_fp32")
+    d = mla_device_inputs(x, w, torch)
+    out, lse = run_mla(lkv, w, d)
+    torch.cuda.synchronize()
+    ro, rl = oracle_mla(oracle, w, x)
+    assert_close(from_dev(out), ro, from_dev(lse), rl, f32=True, what="tiny fp32")
+
+
+@pytest.mark.parametrize("s_q,causal,n_lat", [(1, True, 1), (2, True, 2), (3, False, 1)])
+def test_fp32_variants(lkv, oracle, s_q, causal, n_lat):
+    w, x = small_mla(100 + s_q, B=3, h_q=16, s_q=s_q, n_lat=n_lat, d_c=64, d_rope=16, page=16,
+                     causal=causal, dtype="f32")
+    note(f"case fp32 s_q={s_q} causal={causal} n_lat={n_lat}")
+    d = mla_device_inputs(x, w, torch)
+    out, lse = run_mla(lkv, w, d)
+    ro, rl = oracle_mla(oracle, w, x)
+    assert_close(from_dev(out), ro, from_dev(lse), rl, f32=True, what="fp32")
+
+
+# ------------------------------------------------------------------ bf16 MLA
+@pytest.mark.parametrize("s_q,causal,splits", [
+    (1, True, 0), (1, True, 1), (1, True, 2), (1, True, 7), (1, True, 1000),
+    (2, True, 0), (2, True, 5), (2, False, 3), (3, True, 0)])
+def test_mla_small(lkv, oracle, s_q, causal, splits):
+    w, x = small_mla(200 + 10 * s_q + splits % 97, B=4, s_q=s_q, causal=causal,
+                     seqlens=[1 + (s_q - 1), 63, 65, 700] if s_q < 3 else [3, 64, 129, 400])
+    note(f"case mla_small s_q={s_q} causal={causal} splits={splits} seqlens={list(x['seqlens'])}")
+    d = mla_device_inputs(x, w, torch)
+    out, lse = run_mla(lkv, w, d, x=x if splits % 2 == 0 else None, num_splits=splits)
+    ro, rl = oracle_mla(oracle, w, x)
+    assert_close(from_dev(out), ro, from_dev(lse), rl, what=f"mla s_q={s_q} splits={splits}")
+
+
+def test_mla_split_plans_agree(lkv, oracle):
+    """Forced share counts {1, 2, 7, many} all meet the oracle and agree with
+    each other closely."""
+    w, x = small_mla(250, B=3, s_q=2, seqlens=[900, 31, 444])
+    d = mla_device_inputs(x, w, torch)
+    ro, rl = oracle_mla(oracle, w, x)
+    outs = []
+    for splits in (1, 2, 7, 64):
+        note(f"case split plan {splits}")
+        out, lse = run_mla(lkv, w, d, num_splits=splits)
+        assert_close(from_dev(out), ro, from_dev(lse), rl, what=f"splits={splits}")
+        outs.append(from_dev(out))
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() < 2e-2
+
+
+@pytest.mark.parametrize("h_q,n_lat,d_c", [(32, 2, 256), (16, 1, 512), (64, 1, 128), (48, 1, 512)])
+def test_mla_head_shapes(lkv, oracle, h_q, n_lat, d_c):
+    """GLA-2 (two latent heads, shared RoPE key), few heads (one 16-row tile),
+    a narrow latent, and a head count that leaves a padded row tile."""
+    w, x = small_mla(300 + h_q, B=3, h_q=h_q, n_lat=n_lat, d_c=d_c, seqlens=[77, 300, 129])
+    note(f"case mla_heads h_q={h_q} n_lat={n_lat} d_c={d_c}")
+    d = mla_device_inputs(x, w, torch)
+    out, lse = run_mla(lkv, w, d, x=x)
+    ro, rl = oracle_mla(oracle, w, x)
+    assert_close(from_dev(out), ro, from_dev(lse), rl, what=f"mla h_q={h_q} n_lat={n_lat}")
+
+
+@pytest.mark.parametrize("page", [16, 32, 128, 48])
+def test_mla_page_sizes(lkv, oracle, page):
+    w, x = small_mla(400 + page, B=3, page=page, seqlens=[100, 257, 31])
+    note(f"case page_size={page}")
+    d = mla_device_inputs(x, w, torch)
+    out, lse = run_mla(lkv, w, d, x=x)
+    ro, rl = oracle_mla(oracle, w, x)
+    assert_close(from_dev(out), ro, from_dev(lse), rl, what=f"page={page}")
+
+
+def test_mla_empty_and_short_rows(lkv, oracle):
+    """L_b = 0 (no visible token), L_b < s_q under causal masking (row t=0
+    sees nothing), and L_b = 1: O = 0 / LSE = -inf where nothing is seen."""
+    w, x = small_mla(450, B=4, s_q=2, seqlens=[2, 5, 9, 70])
+    x["seqlens"] = np.array([0, 1, 9, 70], np.int32)
+    note("case empty/short rows")
+    d = mla_device_inputs(x, w, torch)
+    out, lse = run_mla(lkv, w, d, x=x)
+    ro, rl = oracle_mla(oracle, w, x)
+    o, l = from_dev(out), from_dev(lse)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
+    assert np.all(o[1, 0] == 0) and np.all(np.isneginf(l[1, 0]))
+    assert_close(o, ro, l, rl, what="empty/short")
+
+
+def test_batch_zero_is_noop(lkv):
+    q = torch.zeros((0, 1, 128, 512), dtype=torch.bfloat16, device="cuda")
+    qr = torch.zeros((0, 1, 128, 64), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((64, 576), dtype=torch.bfloat16, device="cuda")
+    bt = torch.zeros((0, 1), dtype=torch.int32, device="cuda")
+    sl = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    out, lse = lkv.lkv_mla_decode(q, qr, kv, kv[0, 512:], bt, sl, page_size=64,
+                                  softmax_scale=0.1, kv_tok_stride=576, rope_tok_stride=576)
+    assert out.shape[0] == 0
+
+
+# ------------------------------------------------- block-table indexing, exact
+def test_block_table_one_hot_bit_exact(lkv):
+    """q_nope = 0, q_rope[h] = e_{h mod 64}; k_rope is zero except 2^13 at one
+    chosen token j*(b, d) per RoPE column d.  Every other score is at least
+    340 (natural units) below, so P is exactly one-hot in fp32 and bf16, and
+    the output row must equal the bf16 latent row c_{j*} bit for bit."""
+    w, x = small_mla(500, B=4, s_q=1, seqlens=[700, 64, 65, 1000], table="fragmented")
+    rng = np.random.default_rng(7)
+    x["q_nope"][:] = 0
+    qr = np.zeros(x["q_rope"].shape, np.float32)
+    for h in range(w.h_q):
+        qr[:, :, h, h % w.d_rope] = 1.0
+    x["q_rope"] = li.to_bf16_bits(qr)
+    kv = x["kv"]
+    valid = li.valid_slot_mask(x["block_table"], x["seqlens"], w.page_size, x["num_pages"])
+    kv[..., w.d_c:][valid] = 0
+    target = np.zeros((w.B, w.d_rope), np.int64)
+    big = li.to_bf16_bits(np.array([8192.0], np.float32))[0]
+    for b in range(w.B):
+        L = int(x["seqlens"][b])
+        for dd in range(w.d_rope):
+            j = int(rng.integers(0, L))
+            target[b, dd] = j
+            p, s = x["block_table"][b, j // w.page_size], j % w.page_size
+            kv[p, s, w.d_c + dd] = big
+    note("case one-hot block table")
+    d = mla_device_inputs(x, w, torch)
+    out, _ = run_mla(lkv, w, d, x=x)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b in range(w.B):
+        for h in range(w.h_q):
+            j = target[b, h % w.d_rope]
+            p, s = x["block_table"][b, j // w.page_size], j % w.page_size
+            np.testing.assert_array_equal(got[b, 0, h], kv[p, s, :w.d_c])
+
+
+def test_page_permutation_and_repeat_bit_identical(lkv):
+    w, x = small_mla(510, B=3, s_q=2, seqlens=[500, 130, 64])
+    d = mla_device_inputs(x, w, torch)
+    o1, l1 = run_mla(lkv, w, d, x=x)
+    o1b, l1b = run_mla(lkv, w, d, x=x)
+    perm = np.random.default_rng(3).permutation(x["num_pages"])
+    inv = np.argsort(perm)
+    y = dict(x)
+    y["kv"] = x["kv"][perm].copy()
+    bt = x["block_table"].copy()
+    bt[bt >= 0] = inv[bt[bt >= 0]]
+    y["block_table"] = bt
+    d2 = mla_device_inputs(y, w, torch)
+    o2, l2 = run_mla(lkv, w, d2, x=y)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o1b.view(torch.int16)) and torch.equal(l1, l1b)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------ GQA path
+def _gqa_small(seed, *, B=3, h_q=32, n_kv=8, d_h=128, d_rope=0, s_q=1, seqlens=(100, 700, 65),
+               causal=True):
+    w = li.Workload(name="g", kind="gqa", dtype="bf16", B=B, h_q=h_q, s_q=s_q, page_size=64,
+                    n_kv=n_kv, d_h=d_h, d_rope=d_rope, seqlens=tuple(seqlens), table="shuffled",
+                    causal=causal, scale=1 / math.sqrt(d_h + d_rope), seed=seed)
+    return w, li.generate(w)
+
+
+def _run_gqa(lkv, w, x, **kw):
+    dev = {k: to_dev(x[k], torch) for k in ("q", "k_cache", "v_cache")}
+    qr = to_dev(x["q_rope"], torch) if w.d_rope else None
+    kr = to_dev(x["k_rope"], torch) if w.d_rope else None
+    return lkv.lkv_gqa_decode(dev["q"], qr, dev["k_cache"], dev["v_cache"], kr,
+                              torch.from_numpy(x["block_table"]).cuda(),
+                              torch.from_numpy(x["seqlens"]).cuda(), n_kv=w.n_kv,
+                              page_size=w.page_size, softmax_scale=w.scale, causal=w.causal,
+                              seqlens_host=x["seqlens"], **kw)
+
+
+def _oracle_gqa(oracle, w, x, rows=None):
+    return oracle.gqa_decode(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["seqlens"],
+                             n_kv=w.n_kv, d_h=w.d_h, page_size=w.page_size, scale=w.scale,
+                             causal=w.causal, q_rope=x.get("q_rope"), k_rope=x.get("k_rope"),
+                             d_rope=w.d_rope, rows=rows)
+
+
+@pytest.mark.parametrize("h_q,n_kv,d_h,d_rope,s_q,splits", [
+    (32, 8, 128, 0, 1, 0), (128, 8, 128, 64, 2, 0), (128, 8, 128, 64, 2, 7), (64, 2, 64, 0, 1, 3),
+    (16, 16, 256, 0, 1, 0), (8, 1, 128, 0, 2, 0)])
+def test_gqa_small(lkv, oracle, h_q, n_kv, d_h, d_rope, s_q, splits):
+    w, x = _gqa_small(600 + h_q + d_h, h_q=h_q, n_kv=n_kv, d_h=d_h, d_rope=d_rope, s_q=s_q)
+    note(f"case gqa h_q={h_q} n_kv={n_kv} d_h={d_h} d_rope={d_rope} s_q={s_q} splits={splits}")
+    out, lse = _run_gqa(lkv, w, x, num_splits=splits)
+    ro, rl = _oracle_gqa(oracle, w, x)
+    assert_close(from_dev(out), ro, from_dev(lse), rl, what="gqa")
+
+
+# ------------------------------------------------ expansion and GQLA paths
+def _gqla_small(seed, B=2, seqlens=(130, 64)):
+    w = li.Workload(name="gqla", kind="gqla", dtype="bf16", B=B, h_q=128, s_q=2, page_size=64,
+                    n_lat=1, d_c=512, n_kv=8, d_h=128, d_rope=64, seqlens=tuple(seqlens),
+                    table="shuffled", scale=1 / math.sqrt(192), seed=seed)
+    return w, li.generate(w)
+
+
+def _expand_gpu(lkv, w, x, start_pos=None):
+    kv = to_dev(x["kv"], torch)
+    npg = x["num_pages"]
+    k_out = torch.full((npg, w.page_size, w.n_kv, w.d_h), float("nan"), dtype=torch.bfloat16,
+                       device="cuda")
+    v_out = torch.full_like(k_out, float("nan"))
+    sp = None if start_pos is None else torch.from_numpy(start_pos).cuda()
+    lkv.lkv_gqla_expand_latent(kv.reshape(-1), to_dev(x["w_uk"], torch), to_dev(x["w_uv"], torch),
+                               torch.from_numpy(x["block_table"]).cuda(),
+                               torch.from_numpy(x["seqlens"]).cuda(), k_out, v_out,
+                               page_size=w.page_size, kv_tok_stride=w.d_c + w.d_rope,
+                               start_pos=sp)
+    return kv, k_out, v_out
+
+
+def _w64(x, k):
+    return li.bf16_bits_to_f32(x[k]).astype(np.float64)
+
+
+def test_expand_matches_oracle(lkv, oracle):
+    w, x = _gqla_small(700)
+    note("case expand")
+    _, k_out, v_out = _expand_gpu(lkv, w, x)
+    rk, rv = oracle.expand_latent(x["kv"].reshape(-1), _w64(x, "w_uk"), _w64(x, "w_uv"),
+                                  x["block_table"], x["seqlens"], page_size=w.page_size,
+                                  num_pages=x["num_pages"], kv_tok_stride=w.d_c + w.d_rope)
+    valid = li.valid_slot_mask(x["block_table"], x["seqlens"], w.page_size, x["num_pages"])
+    for got, ref in ((from_dev(k_out), rk), (from_dev(v_out), rv)):
+        g, r = got[valid], ref[valid]
+        # fp32 accumulation, one bf16 rounding: within 2 bf16 ulps of the fp64 value
+        tol = 2 * 2.0 ** -8 * np.abs(r) + 1e-6
+        assert (np.abs(g - r) <= tol).all(), float(np.abs(g - r).max())
+        assert np.isnan(got[~valid]).all(), "rows of invalid tokens were written"
+
+
+def test_expand_start_pos(lkv):
+    w, x = _gqla_small(701)
+    sp = np.array([70, 0], np.int32)
+    _, k_out, _ = _expand_gpu(lkv, w, x, start_pos=sp)
+    k = from_dev(k_out)
+    bt = x["block_table"]
+    for j in (0, 69):
+        assert np.isnan(k[bt[0, j // 64], j % 64]).all()
+    assert np.isfinite(k[bt[0, 70 // 64], 70 % 64]).all()
+    assert np.isfinite(k[bt[1, 0], 0]).all()
+
+
+def test_gqla_grouped_and_absorbed_paths(lkv, oracle):
+    """GQLA section 2: the same weights give two paths.  GPU grouped path
+    (expansion kernel, then grouped decode over the bf16 K/V) and GPU
+    absorbed path (latent decode with q' = W_UK q, then W_UV) both match the
+    oracle's grouped path, and each other."""
+    w, x = _gqla_small(702)
+    note("case gqla paths")
+    kv, k_out, v_out = _expand_gpu(lkv, w, x)
+    q_h = li.bf16_bits_to_f32(x["q_nope_h"]).astype(np.float64)
+    q_r = x["q_rope"]
+    flat = kv.reshape(-1)
+    out_g, lse_g = lkv.lkv_gqa_decode(to_dev(x["q_nope_h"], torch), to_dev(q_r, torch), k_out,
+                                      v_out, flat[w.d_c:], torch.from_numpy(x["block_table"]).cuda(),
+                                      torch.from_numpy(x["seqlens"]).cuda(), n_kv=w.n_kv,
+                                      page_size=w.page_size, softmax_scale=w.scale,
+                                      rope_tok_stride=w.d_c + w.d_rope, seqlens_host=x["seqlens"])
+    wuk, wuv = _w64(x, "w_uk"), _w64(x, "w_uv")
+    rk, rv = oracle.expand_latent(x["kv"].reshape(-1), wuk, wuv, x["block_table"], x["seqlens"],
+                                  page_size=w.page_size, num_pages=x["num_pages"],
+                                  kv_tok_stride=w.d_c + w.d_rope)
+    rk, rv = np.nan_to_num(rk), np.nan_to_num(rv)
+    kv64 = li.bf16_bits_to_f32(x["kv"]).astype(np.float64)
+    ro, rl = oracle.gqa_decode(q_h, rk, rv, x["block_table"], x["seqlens"], n_kv=w.n_kv, d_h=w.d_h,
+                               page_size=w.page_size, scale=w.scale,
+                               q_rope=li.bf16_bits_to_f32(q_r).astype(np.float64),
+                               k_rope=np.nan_to_num(kv64[..., w.d_c:]).copy(), d_rope=w.d_rope)
+    assert_close(from_dev(out_g), ro, from_dev(lse_g), rl, what="gqla grouped (GPU) vs oracle")
+    # absorbed path: q' from the oracle's absorb step, rounded to bf16 as the input
+    qa = oracle.absorb_query(q_h, wuk)
+    qa_bits = li.to_bf16_bits(qa.astype(np.float32))
+    dev = dict(q_nope=to_dev(qa_bits, torch), q_rope=to_dev(q_r, torch))
+    out_a, lse_a = lkv.lkv_mla_decode(dev["q_nope"], dev["q_rope"], flat, flat[w.d_c:],
+                                      torch.from_numpy(x["block_table"]).cuda(),
+                                      torch.from_numpy(x["seqlens"]).cuda(), page_size=w.page_size,
+                                      softmax_scale=w.scale, kv_tok_stride=w.d_c + w.d_rope,
+                                      rope_tok_stride=w.d_c + w.d_rope, seqlens_host=x["seqlens"])
+    o_abs = oracle.up_project(from_dev(out_a), wuv)
+    assert_close(o_abs, ro, from_dev(lse_a), rl, what="gqla absorbed (GPU) + W_UV vs oracle grouped")
+
+
+# ------------------------------------------------------------ split combine
+def test_split_combine_entry_point(lkv, oracle):
+    rng = np.random.default_rng(800)
+    B, s_q, h_q, dv = 4, 2, 16, 512
+    counts = [3, 0, 1, 5]
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    n = int(offs[-1])
+    o_part = rng.standard_normal((n, s_q, h_q, dv)).astype(np.float32)
+    lse_part = (rng.standard_normal((n, s_q, h_q)) * 3).astype(np.float32)
+    lse_part[0, 0, :4] = -np.inf          # an empty split inside a sequence
+    lse_part[1:3, 1, 2] = -np.inf
+    ro, rl = oracle.lse_combine(o_part.astype(np.float64), lse_part.astype(np.float64), offs)
+    for dt in (torch.float32, torch.bfloat16):
+        note(f"case combine {dt}")
+        out, lse = lkv.lkv_split_combine(torch.from_numpy(o_part).cuda(),
+                                         torch.from_numpy(lse_part).cuda(),
+                                         torch.from_numpy(offs).cuda(), dtype=dt)
+        assert_close(from_dev(out), ro, from_dev(lse), rl, f32=dt == torch.float32,
+                     what=f"combine {dt}")
+
+
+# ------------------------------------------------------- full-size workloads
+FULL = [("dsv3_mla_b64_l4096", 96), ("gla2_b128_l8192", 64), ("ragged_mla_b16_sq1", 48),
+        ("ragged_mla_b16_sq2", 48)]
+
+
+@pytest.mark.parametrize("name,nrows", FULL)
+def test_full_size_mla_sampled(lkv, oracle, name, nrows):
+    w = li.workload(name)
+    note(f"case full {name}: generating inputs")
+    x = li.generate(w)
+    d = mla_device_inputs(x, w, torch)
+    note(f"case full {name}: running GPU")
+    out, lse = run_mla(lkv, w, d, x=x)
+    torch.cuda.synchronize()
+    rows = li.sample_rows(11, w.B, w.s_q, w.h_q, nrows)
+    ro, rl = oracle_mla(oracle, w, x, rows=rows)
+    got, gl = from_dev(out), from_dev(lse)
+    assert np.isfinite(got).all() and np.isfinite(gl).all()
+    assert_close(rows_of(got, rows), rows_of(ro, rows), rows_of(gl, rows), rows_of(rl, rows),
+                 what=name)
+
+
+def test_full_size_gqa_sampled(lkv, oracle):
+    w = li.workload("gqa_b128_l8192")
+    note("case full gqa_b128_l8192: generating inputs")
+    x = li.generate(w)
+    out, lse = _run_gqa(lkv, w, x)
+    torch.cuda.synchronize()
+    rows = li.sample_rows(12, w.B, w.s_q, w.h_q, 64)
+    ro, rl = _oracle_gqa(oracle, w, x, rows=rows)
+    got, gl = from_dev(out), from_dev(lse)
+    assert np.isfinite(got).all()
+    assert_close(rows_of(got, rows), rows_of(ro, rows), rows_of(gl, rows), rows_of(rl, rows),
+                 what="gqa full")
+
+
+def test_full_size_gqla_grouped_sampled(lkv, oracle):
+    w = li.workload("gqla_grouped_b64_l4096_sq2")
+    note("case full gqla: generating inputs")
+    x = li.generate(w)
+    kv, k_out, v_out = _expand_gpu(lkv, w, x)
+    flat = kv.reshape(-1)
+    out, lse = lkv.lkv_gqa_decode(to_dev(x["q_nope_h"], torch), to_dev(x["q_rope"], torch), k_out,
+                                  v_out, flat[w.d_c:], torch.from_numpy(x["block_table"]).cuda(),
+                                  torch.from_numpy(x["seqlens"]).cuda(), n_kv=w.n_kv,
+                                  page_size=w.page_size, softmax_scale=w.scale,
+                                  rope_tok_stride=w.d_c + w.d_rope, seqlens_host=x["seqlens"])
+    torch.cuda.synchronize()
+    # oracle grouped path on rows sampled from the first and the last
+    # sequence: fp64 expansion of just those sequences' tokens (their pages
+    # copied into a compact pool), then O3 on the sampled rows
+    seqs = [0, w.B - 1]
+    per = w.s_q * w.h_q
+    rng = np.random.default_rng(13)
+    rows = np.sort(np.concatenate([s * per + rng.choice(per, 16, replace=False) for s in seqs]))
+    rows = rows.astype(np.int32)
+    pages = [x["block_table"][s, : (int(x["seqlens"][s]) + 63) // 64] for s in seqs]
+    sub_bt = np.full((2, x["block_table"].shape[1]), -1, np.int32)
+    pool = []
+    for i, pg in enumerate(pages):
+        sub_bt[i, : len(pg)] = np.arange(len(pool), len(pool) + len(pg))
+        pool.extend(pg.tolist())
+    sub_kv = x["kv"][np.array(pool)]
+    sub_sl = x["seqlens"][seqs]
+    wuk, wuv = _w64(x, "w_uk"), _w64(x, "w_uv")
+    rk, rv = oracle.expand_latent(sub_kv.reshape(-1), wuk, wuv, sub_bt, sub_sl,
+                                  page_size=w.page_size, num_pages=len(pool),
+                                  kv_tok_stride=w.d_c + w.d_rope)
+    kr64 = li.bf16_bits_to_f32(sub_kv[..., w.d_c:]).astype(np.float64)
+    q_h = li.bf16_bits_to_f32(x["q_nope_h"]).astype(np.float64)[seqs]
+    q_r = li.bf16_bits_to_f32(x["q_rope"]).astype(np.float64)[seqs]
+    sub_rows = np.array([seqs.index(int(r) // per) * per + int(r) % per for r in rows], np.int32)
+    note("case full gqla: oracle")
+    ro, rl = oracle.gqa_decode(q_h, np.nan_to_num(rk), np.nan_to_num(rv), sub_bt, sub_sl,
+                               n_kv=w.n_kv, d_h=w.d_h, page_size=w.page_size, scale=w.scale,
+                               q_rope=q_r, k_rope=np.nan_to_num(kr64), d_rope=w.d_rope,
+                               rows=sub_rows)
+    got, gl = from_dev(out), from_dev(lse)
+    assert np.isfinite(got).all()
+    assert_close(rows_of(got, rows), rows_of(ro, sub_rows), rows_of(gl, rows), rows_of(rl, sub_rows),
+                 what="gqla grouped full")
