@@ -34,6 +34,8 @@
 //   PV:     wave w computes O^T = V^T P^T for its quarter of the value
 //           width; V^T comes straight from the token-major tile through
 //           ds_read_b64_tr_b16, P^T through LDS as bf16.
+#include <type_traits>
+
 #include "lkv_internal.h"
 
 namespace lkv {
@@ -53,14 +55,109 @@ constexpr float kLn2 = 0.693147180559945309f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
-// 16-byte chunk `chunk` of LDS row `row` lives at chunk slot chunk ^ sig(row),
-// sig(t) = 2*(t mod 4) + (t mod 8) / 4.  Eight consecutive rows reading one
-// chunk hit eight different bank groups, and four consecutive rows reading a
-// pair of chunks (the transpose read) do too.
+// LDS swizzle.  The LDS has 64 banks of 4 bytes: a b128 read is served 16
+// lanes per cycle and a b64 transpose read 32 lanes per cycle, 256 bytes each.
+// Chunk `chunk` (16 bytes) of row `row` of a region with CPR chunks per row
+// lives at chunk slot swz<CPR>(chunk, row):
+//   CPR >= 16: chunk ^ h(row), h a bijection of row mod 16 with
+//              h = 2*(row mod 4) + 8*bit3(row) + bit2(row).  Sixteen
+//              consecutive rows reading one chunk hit sixteen different
+//              256-byte bank slots, and the transpose read (rows r..r+3 and
+//              r+8..r+11, a pair of chunks each) does too.
+//   CPR == 8:  chunk ^ ((row / 2) mod 8): two 128-byte rows share a bank
+//              window, so the XOR follows the row pair index.
+// Row lengths are multiples of 256 bytes (CPR >= 16) or exactly 128 bytes.
+template <int CPR>
 __device__ __forceinline__ int swz(int chunk, int row) {
-  const int t = row & 7;
-  return chunk ^ (((t & 3) << 1) | (t >> 2));
+  static_assert(CPR == 8 || CPR % 16 == 0, "region row length");
+  if constexpr (CPR >= 16) return chunk ^ (((row & 3) << 1) | (row & 8) | ((row >> 2) & 1));
+  else return chunk ^ ((row >> 1) & 7);
 }
+
+// Direct global -> LDS staging of one tile region (64 tokens x CPT 16-byte
+// chunks).  One wave instruction fills 1 KiB of LDS (64 lanes x 16 bytes, in
+// lane order) with 64 / CPT whole token rows; lane i fetches the chunk whose
+// swizzled slot is i, so the XOR layout costs nothing at store time.
+// row_reg: lane t holds the cache row of token t of the tile.
+template <int CPT>
+__device__ __forceinline__ void dma_region(const bf16 *gbase, long long stride, bf16 *region,
+                                           int row_reg, int w, int lane) {
+  static_assert(CPT >= 8 && CPT <= 64 && CPT % 8 == 0, "chunks per token");
+  constexpr int TPI = 64 / CPT;
+#pragma unroll
+  for (int u = 0; u < CPT / 4; ++u) {
+    const int t0 = (u * 4 + w) * TPI;
+    int tok, row;
+    if constexpr (CPT == 64) {
+      tok = t0;
+      row = __builtin_amdgcn_readlane(row_reg, t0);
+    } else {
+      tok = t0 + lane / CPT;
+      row = __shfl(row_reg, tok);
+    }
+    const int ch = swz<CPT>(lane % CPT, tok);
+    const bf16 *src = gbase + (long long)row * stride + ch * 8;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(region + t0 * CPT * 8),
+                                     16, 0, 0);
+  }
+}
+
+// As dma_region, for a tile whose token t sits at row base + t (whole tile on
+// one page).  Addresses are a wave-uniform 64-bit base (scalar registers)
+// plus a per-lane 32-bit byte offset that depends only on the parity of the
+// instruction index, so the loop issues loads with no per-load vector math.
+//   wu    wave index, known uniform
+//   loff  per-lane byte offsets for even / odd instruction index
+template <int CPT>
+struct ContigDma {
+  static constexpr int TPI = 64 / CPT;
+  int loff[4];  // by instruction index mod 4 (the swizzle sees row mod 16)
+  __device__ __forceinline__ void init(long long stride, int wu, int lane) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t0 = (4 * v + wu) * TPI;
+      const int tin = lane / CPT, tok = t0 + tin;
+      loff[v] = tin * (int)stride * 2 + swz<CPT>(lane % CPT, tok) * 16;
+    }
+  }
+  __device__ __forceinline__ void issue(const bf16 *base, long long stride, bf16 *region, int wu) const {
+    const char *bw = reinterpret_cast<const char *>(base) + (long long)(wu * TPI) * stride * 2;
+    bf16 *rw = region + wu * TPI * CPT * 8;
+#pragma unroll
+    for (int u = 0; u < CPT / 4; ++u) {
+      const char *src = bw + (long long)(4 * u * TPI) * stride * 2 + loff[u & 3];
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(rw + 4 * u * TPI * CPT * 8),
+                                       16, 0, 0);
+    }
+  }
+};
+
+// Cross-lane partners l ^ 16 and l ^ 32 through the gfx950 permlane swaps
+// (VALU, no LDS round trip).
+__device__ __forceinline__ float xlane_max16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xlane_max32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xlane_sum16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]) - v;
+}
+__device__ __forceinline__ float xlane_sum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]) - v;
+}
+
+// The softmax reference maximum moves only when a tile's maximum exceeds it by
+// more than this (base-2 units), so O and the row sums are rescaled rarely;
+// probabilities stay below 2^kLazy, well inside fp32 and bf16 range.
+constexpr float kLazy = 8.0f;
+
+// s_waitcnt vmcnt(0): every direct-to-LDS load of this wave has landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ s16x4 lds_read_tr(const bf16 *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
@@ -127,20 +224,19 @@ __device__ bool plan_share(const int32_t *seqlens, int B, int C, int c, int *sh,
 template <int DK, int DR, int DV, bool VA, int ROWS>
 struct Cfg {
   static constexpr int KW = DK + DR;
-  static_assert(KW % 64 == 0 && DV % 64 == 0, "widths must be multiples of 64");
+  static_assert(DK % 64 == 0 && DR % 64 == 0 && DV % 64 == 0, "widths must be multiples of 64");
   static_assert(!VA || DV == DK, "the latent is the value");
-  static constexpr int KSTR = KW;                        // LDS row stride of the key tile
-  static constexpr int VSTR = VA ? KW : DV;              // LDS row stride of the value tile
-  static constexpr int KTILE = kTile * KSTR;
-  static constexpr int BUF = KTILE + (VA ? 0 : kTile * DV);
+  // LDS tile buffer: key main part [64][DK], RoPE key [64][DR], and for
+  // separate values [64][DV]; every region row is a multiple of 128 bytes.
+  static constexpr int ROFF = kTile * DK;                // RoPE region offset (elements)
+  static constexpr int VOFF = ROFF + kTile * DR;         // value region offset
+  static constexpr int VSTR = DV;
+  static constexpr int BUF = VOFF + (VA ? 0 : kTile * DV);
   static constexpr int KS = KW / 32;                     // k-steps of QK^T
   static constexpr int KSN = DK / 32;                    // of which on the main part
   static constexpr int NT = ROWS / 16;
   static constexpr int DVW = DV / kWaves;
   static constexpr int MT = DVW / 16;
-  static constexpr int KC8 = KW / 64;                    // key chunks per thread per token
-  static constexpr int VC8 = VA ? 0 : DV / 64;
-  static constexpr int NLD = 2 * (KC8 + VC8);
   static constexpr int PSTR = kTile + 8;                 // P row stride (elements)
   static constexpr int LDS_BYTES = 2 * BUF * 2 + ROWS * PSTR * 2 + kWaves * ROWS * 4 + 64;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -150,7 +246,11 @@ template <int DK, int DR, int DV, bool VA, int ROWS>
 __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodeParams p) {
   using C = Cfg<DK, DR, DV, VA, ROWS>;
   constexpr int NT = C::NT, MT = C::MT, KS = C::KS;
-  __shared__ __attribute__((aligned(16))) bf16 s_buf[2 * C::BUF];
+  // two tile buffers as distinct LDS objects: the compiler can then prove
+  // that direct-to-LDS loads into one never alias reads of the other and
+  // keeps the prefetch in flight across the whole tile
+  __shared__ __attribute__((aligned(16))) bf16 s_buf0[C::BUF];
+  __shared__ __attribute__((aligned(16))) bf16 s_buf1[C::BUF];
   __shared__ __attribute__((aligned(16))) bf16 s_p[ROWS * C::PSTR];
   __shared__ float s_red[kWaves * ROWS];
   __shared__ int s_plan[8];
@@ -175,7 +275,45 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
   const bf16 *__restrict__ kc = static_cast<const bf16 *>(p.k) + (long long)kvh * DK;
   const bf16 *__restrict__ rc = static_cast<const bf16 *>(p.r);
   const bf16 *__restrict__ vc = static_cast<const bf16 *>(p.v) + (long long)kvh * DV;
-  const int tk0 = tid >> 3, tk1 = tk0 + 32, cl = tid & 7;
+  // a 64-token tile never straddles a page when pages are a power of two >= 64
+  const bool aligned_pages = p.page_shift >= 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  ContigDma<DK / 8> dk_;
+  ContigDma<(DR > 0 ? DR : 64) / 8> dr_;
+  ContigDma<DV / 8> dv_;
+  dk_.init(p.k_stride, wu, lane);
+  if constexpr (DR > 0) dr_.init(p.r_stride, wu, lane);
+  if constexpr (!VA) dv_.init(p.v_stride, wu, lane);
+
+  // Per-lane LDS element offsets of the fragment reads; the rest of each
+  // address is a compile-time immediate.
+  //  key (QK^T A operand): row tok = 16w + n, chunk 4ks + g.  The swizzle
+  //    changes the low four chunk bits only, so the slot is
+  //    16*(ks/4) + ((4*(ks%4) + g) ^ h(tok)) for the main part and
+  //    (4*(ks%2) + g) ^ h8(tok) for the 8-chunk RoPE rows.
+  int koff[4], roff[2];
+  {
+    const int tok = 16 * w + n;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) koff[e] = tok * DK + swz<DK / 8>(4 * e + g, tok) * 8;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      roff[e] = DR > 0 ? tok * DR + swz<(DR > 0 ? DR : 64) / 8>(4 * e + g, tok) * 8 : 0;
+  }
+  //  value (transpose read): rows rv = 8g + n/4 (+4), value column block mt of
+  //    this wave -> chunk w*DVW/8 + 2mt + (n%4)/2, element (n%2)*4
+  int voff[2][MT];
+  {
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      const int rv = 8 * g + (n >> 2) + 4 * hlf;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int ch = w * C::DVW / 8 + 2 * mt + ((n & 3) >> 1);
+        voff[hlf][mt] = rv * C::VSTR + swz<DV / 8>(ch, rv) * 8 + 4 * (n & 1);
+      }
+    }
+  }
 
   while (cu < t1) {
     const int L = p.seqlens[b];
@@ -190,7 +328,8 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
     }
     const int32_t *bt = p.block_table + (long long)b * p.max_pages;
 
-    // ---- the query rows of this work-group
+    // ---- the query rows of this work-group.  Padded rows (past the last
+    // query row) compute on a zero query and are never written.
     int lim[NT], rowid[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -200,10 +339,13 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
         lim[nt] = p.causal ? L - p.s_q + t + 1 : L;
         rowid[nt] = (b * p.s_q + t) * p.h_q + h;
       } else {
-        lim[nt] = 0;
+        lim[nt] = L;
         rowid[nt] = -1;
       }
     }
+    // every row of the work-group sees at least lim_min tokens: tiles below
+    // it need no mask
+    const int lim_min = p.causal ? L - p.s_q + (rt * ROWS) / p.hpk + 1 : L;
     bf16x8 qreg[KS][NT];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -223,6 +365,9 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) oacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // m_run: the reference maximum (base 2) of each row; probabilities are
+    // exp2(x - m_run) and may exceed 1 by up to 2^kLazy before O and the
+    // sums are rescaled to a new reference.
     float m_run[NT], l_part[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -230,131 +375,144 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
       l_part[nt] = 0.f;
     }
 
-    // cache row of token tk of tile `tile`, -1 past the sequence
-    auto token_row = [&](int tile, int tk) -> int {
-      const int j = tile * kTile + tk;
-      if (j >= L) return -1;
-      int pg, sl;
-      if (p.page_shift >= 0) {
-        pg = bt[j >> p.page_shift];
-        sl = j & (p.page_size - 1);
+    // Block-table window: lane i of every wave holds the page id of logical
+    // page win + i of this sequence (-1 past its last page).  It is refilled
+    // only at the top of an iteration, when no tile load is in flight.
+    const int npages = L > 0 ? (L + p.page_size - 1) / p.page_size : 0;
+    int win = -(1 << 30), btw = -1;
+    auto page_of = [&](int j) -> int { return p.page_shift >= 0 ? j >> p.page_shift : j / p.page_size; };
+    auto slot_of = [&](int j) -> int {
+      return p.page_shift >= 0 ? j & (p.page_size - 1) : j % p.page_size;
+    };
+    auto ensure_window = [&](int lo, int hi) {
+      if (lo < win || hi >= win + 64) {
+        win = lo;
+        btw = win + lane < npages ? bt[win + lane] : -1;
+      }
+    };
+    const int row_first = L > 0 ? bt[0] * p.page_size : 0;
+
+    auto load_tile = [&](int tile, bf16 *buf) {
+      const int jb = tile * kTile;
+      if (aligned_pages && jb + kTile <= L) {
+        // whole tile valid and inside one page: token t sits at row row0 + t
+        const int pi = jb >> p.page_shift;
+        ensure_window(pi, pi);
+        const int pg = __builtin_amdgcn_readlane(btw, pi - win);
+        const long long row0 = (long long)pg * p.page_size + (jb & (p.page_size - 1));
+        dk_.issue(kc + row0 * p.k_stride, p.k_stride, buf, wu);
+        if constexpr (DR > 0) dr_.issue(rc + row0 * p.r_stride, p.r_stride, buf + C::ROFF, wu);
+        if constexpr (!VA) dv_.issue(vc + row0 * p.v_stride, p.v_stride, buf + C::VOFF, wu);
       } else {
-        pg = bt[j / p.page_size];
-        sl = j % p.page_size;
-      }
-      return pg * p.page_size + sl;
-    };
-
-    u32x4 pre[C::NLD];
-    auto load_tile = [&](int r0, int r1) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int row = u ? r1 : r0;
-#pragma unroll
-        for (int k = 0; k < C::KC8; ++k) {
-          const int ch = cl + 8 * k;
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (row >= 0) {
-            const bf16 *src = ch < DK / 8 ? kc + (long long)row * p.k_stride + 8 * ch
-                                          : rc + (long long)row * p.r_stride + 8 * (ch - DK / 8);
-            v = *reinterpret_cast<const u32x4 *>(src);
-          }
-          pre[u * (C::KC8 + C::VC8) + k] = v;
-        }
-#pragma unroll
-        for (int k = 0; k < C::VC8; ++k) {
-          const int ch = cl + 8 * k;
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (row >= 0) v = *reinterpret_cast<const u32x4 *>(vc + (long long)row * p.v_stride + 8 * ch);
-          pre[u * (C::KC8 + C::VC8) + C::KC8 + k] = v;
-        }
-      }
-    };
-    auto store_tile = [&](int bi) {
-      bf16 *kt = s_buf + bi * C::BUF;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int tok = u ? tk1 : tk0;
-#pragma unroll
-        for (int k = 0; k < C::KC8; ++k) {
-          const int ch = cl + 8 * k;
-          *reinterpret_cast<u32x4 *>(kt + tok * C::KSTR + swz(ch, tok) * 8) =
-              pre[u * (C::KC8 + C::VC8) + k];
-        }
-#pragma unroll
-        for (int k = 0; k < C::VC8; ++k) {
-          const int ch = cl + 8 * k;
-          *reinterpret_cast<u32x4 *>(kt + C::KTILE + tok * C::VSTR + swz(ch, tok) * 8) =
-              pre[u * (C::KC8 + C::VC8) + C::KC8 + k];
-        }
+        // general path: lane t computes the row of token t; tokens past the
+        // sequence read token 0's row (valid, finite; their weight is 0)
+        ensure_window(page_of(jb), page_of(max(jb, min(jb + kTile, L) - 1)));
+        const int j = jb + lane;
+        const int pg = __shfl(btw, (page_of(j) - win) & 63);
+        const int rr = j < L ? pg * p.page_size + slot_of(j) : row_first;
+        dma_region<DK / 8>(kc, p.k_stride, buf, rr, w, lane);
+        if constexpr (DR > 0) dma_region<DR / 8>(rc, p.r_stride, buf + C::ROFF, rr, w, lane);
+        if constexpr (!VA) dma_region<DV / 8>(vc, p.v_stride, buf + C::VOFF, rr, w, lane);
       }
     };
 
-    // ---- pipeline prologue
-    load_tile(token_row(lt0, tk0), token_row(lt0, tk1));
-    store_tile(0);
-    int nx0 = -1, nx1 = -1;
-    if (lt0 + 1 < lt1) {
-      nx0 = token_row(lt0 + 1, tk0);
-      nx1 = token_row(lt0 + 1, tk1);
+    // ---- pipeline prologue.  The wait also retires the query loads, so no
+    // wait for them is left inside the tile loop (where it would drain the
+    // prefetch of the next tile as well).
+    if (L > 0) {
+      load_tile(lt0, s_buf0);
+      wait_vmem();
+    } else {
+      wait_vmem();
+      // empty sequence: one all-masked tile of zeros
+      for (int i = tid; i < C::BUF / 8; i += kThreads)
+        *reinterpret_cast<u32x4 *>(s_buf0 + 8 * i) = u32x4{0u, 0u, 0u, 0u};
     }
+    // Make the compiler's wait for the query loads happen here, once per
+    // sequence: an empty asm statement that reads every query register
+    // forces it.  Otherwise the wait lands at the first MFMA inside the tile
+    // loop, every tile, where it would also drain the prefetch of the next
+    // tile.
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(qreg[ks][nt]));
     __syncthreads();
 
-    for (int it = lt0; it < lt1; ++it) {
-      const int bi = (it - lt0) & 1;
+    // one tile; BI (compile time) names the buffer it reads, the other one
+    // receives the next tile
+    auto step = [&](auto bi_tag, int it) {
+      constexpr int BI = decltype(bi_tag)::value;
+      bf16 *const kt = BI == 0 ? s_buf0 : s_buf1;
+      bf16 *const nxt = BI == 0 ? s_buf1 : s_buf0;
       const bool has_next = it + 1 < lt1;
-      if (has_next) load_tile(nx0, nx1);
-      int nn0 = -1, nn1 = -1;
-      if (it + 2 < lt1) {
-        nn0 = token_row(it + 2, tk0);
-        nn1 = token_row(it + 2, tk1);
-      }
-      const bf16 *kt = s_buf + bi * C::BUF;
+      if (has_next) load_tile(it + 1, nxt);
 
-      // ---- S^T = K Q^T for tokens 16w..16w+15
+      // ---- S^T = K Q^T for tokens 16w..16w+15; every key fragment is read
+      // before the first MFMA so the LDS latency is paid once per tile
       f32x4 sacc[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
       {
-        const int tok = 16 * w + n;
-        const bf16 *krow = kt + tok * C::KSTR;
+        bf16x8 kf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(krow + swz(4 * ks + g, tok) * 8);
+          // chunk 4ks + g of row tok: slot 8(ks/2) + ((4(ks%2) + g) ^ sig)
+          const bf16 *src = ks < C::KSN ? kt + koff[ks & 3] + 128 * (ks >> 2)
+                                        : kt + C::ROFF + roff[(ks - C::KSN) & 1];
+          kf[ks] = *reinterpret_cast<const bf16x8 *>(src);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, KS * NT, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
-            sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[ks][nt], sacc[nt], 0, 0, 0);
-        }
+            sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qreg[ks][nt], sacc[nt], 0, 0, 0);
       }
 
-      // ---- mask, tile maximum
-      const int tokb = it * kTile + 16 * w + 4 * g;
+      // ---- scale, mask (only on tiles that cross a row's visible length),
+      // tile maximum per row over this wave's 16 tokens
       float x[NT][4];
+      const bool need_mask = (it + 1) * kTile > lim_min;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[nt][i] = sacc[nt][i] * p.scale_log2;
+      if (need_mask) {
+        const int tokb = it * kTile + 16 * w + 4 * g;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (tokb + i >= lim[nt]) x[nt][i] = neg_inf();
+      }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        float mx = neg_inf();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[nt][i] = (tokb + i < lim[nt]) ? sacc[nt][i] * p.scale_log2 : neg_inf();
-          mx = fmaxf(mx, x[nt][i]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        float mx = fmaxf(fmaxf(x[nt][0], x[nt][1]), fmaxf(x[nt][2], x[nt][3]));
+        mx = fmaxf(mx, xlane_max16(mx));
+        mx = fmaxf(mx, xlane_max32(mx));
         if (g == 0) s_red[w * ROWS + 16 * nt + n] = mx;
       }
       __syncthreads();
 
-      // ---- online softmax, P^T -> LDS (bf16)
+      // ---- online softmax with a lazily moved reference maximum
+      bool moved = false;
       float alpha[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         float mt = s_red[16 * nt + n];
 #pragma unroll
         for (int v = 1; v < kWaves; ++v) mt = fmaxf(mt, s_red[v * ROWS + 16 * nt + n]);
-        const float mnew = fmaxf(m_run[nt], mt);
-        const float muse = mnew == neg_inf() ? 0.f : mnew;
-        alpha[nt] = __builtin_amdgcn_exp2f(m_run[nt] - muse);
-        m_run[nt] = mnew;
+        // move the reference only when this tile's maximum exceeds it by more
+        // than kLazy (or it is still -inf); all waves decide alike per row
+        alpha[nt] = 1.f;
+        if (mt > m_run[nt] + kLazy) {
+          alpha[nt] = __builtin_amdgcn_exp2f(m_run[nt] - mt);
+          m_run[nt] = mt;
+          moved = true;
+        }
+        const float muse = m_run[nt] == neg_inf() ? 0.f : m_run[nt];
         bf16x4 pv;
         float sum = 0.f;
 #pragma unroll
@@ -366,37 +524,49 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
         l_part[nt] = l_part[nt] * alpha[nt] + sum;
         *reinterpret_cast<bf16x4 *>(s_p + (16 * nt + n) * C::PSTR + 16 * w + 4 * g) = pv;
       }
+      // rescale O only when some row of this wave moved its reference
+      if (__builtin_amdgcn_ballot_w64(moved)) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) oacc[mt][nt] *= alpha[nt];
+      }
       __syncthreads();
 
       // ---- O^T = V^T P^T on this wave's value columns
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) oacc[mt][nt] *= alpha[nt];
-      const bf16 *vt = VA ? kt : kt + C::KTILE;
+      const bf16 *vt = VA ? kt : kt + C::VOFF;
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         bf16x8 pb[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           pb[nt] = *reinterpret_cast<const bf16x8 *>(s_p + (16 * nt + n) * C::PSTR + 32 * k2 + 8 * g);
-        const int rv = 32 * k2 + 8 * g + (n >> 2);
+        s16x4 vlo[MT], vhi[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const int dim = w * C::DVW + 16 * mt + 4 * (n & 3);
-          const int ch = dim >> 3, off = dim & 7;
-          const s16x4 lo = lds_read_tr(vt + rv * C::VSTR + swz(ch, rv) * 8 + off);
-          const s16x4 hi = lds_read_tr(vt + (rv + 4) * C::VSTR + swz(ch, rv + 4) * 8 + off);
-          const bf16x8 a = join(lo, hi);
+          // rows rv and rv + 4 (+32 per k2), chunk pair of value column block mt
+          const int imm = 32 * k2 * C::VSTR;
+          vlo[mt] = lds_read_tr(vt + voff[0][mt] + imm);
+          vhi[mt] = lds_read_tr(vt + voff[1][mt] + imm);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, NT + 2 * MT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MT * NT, 0);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const bf16x8 a = join(vlo[mt], vhi[mt]);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
             oacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nt], oacc[mt][nt], 0, 0, 0);
         }
       }
-      if (has_next) store_tile(bi ^ 1);
-      nx0 = nn0;
-      nx1 = nn1;
+      // unconditional: a wait that only some paths take would leave the
+      // compiler assuming a load may still be in flight into the next step
+      wait_vmem();
       __syncthreads();
+    };
+    for (int it = lt0; it < lt1; it += 2) {
+      step(std::integral_constant<int, 0>{}, it);
+      if (it + 1 < lt1) step(std::integral_constant<int, 1>{}, it + 1);
     }
 
     // ---- row sums over lanes and waves, finalize
@@ -404,8 +574,8 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float v = l_part[nt];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
+      v += xlane_sum16(v);
+      v += xlane_sum32(v);
       if (g == 0) s_red[w * ROWS + 16 * nt + n] = v;
     }
     __syncthreads();

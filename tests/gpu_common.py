@@ -57,7 +57,7 @@ def assert_close(out, ref, lse=None, lse_ref=None, *, f32=False, what=""):
         lse = np.asarray(lse, np.float64)
         lse_ref = np.asarray(lse_ref, np.float64)
         both_inf = np.isneginf(lse) & np.isneginf(lse_ref)
-        d = np.abs(np.where(both_inf, 0.0, lse - lse_ref))
+        d = np.abs(np.where(both_inf, 0.0, np.where(both_inf, 0.0, lse) - np.where(both_inf, 0.0, lse_ref)))
         ml = float(d.max()) if d.size else 0.0
         note(f"  {what}: lse max_abs={ml:.3e}")
         assert ml <= (1e-5 if f32 else LSE_MAX_ABS), f"{what}: LSE error {ml}"
