@@ -11,9 +11,15 @@ a 512-wide latent plus a 64-wide shared RoPE key, 4096 cache tokens each,
 64-token pages, shuffled block table, bf16 with fp32 accumulation.
 
 Timing: W untimed warm-up steps, then K timed steps bracketed by device
-synchronisation; HIP events on the stream the library launches on time each
-launch.  Four independent copies of the cache rotate from step to step so
-that the 256 MB Infinity Cache cannot hold the working set.
+synchronisation.  HIP events on the stream the library launches on time each
+step (attention kernel + split-KV combine), and a second pair, recorded by the
+library itself around the attention kernel (kernel_events), times that kernel
+alone for the roofline.  Four independent copies of the cache rotate from step
+to step so that the 256 MB Infinity Cache cannot hold the working set.
+
+    python bench.py --calibrate-copy
+runs only a plain device-to-device copy of a known size (for scaling the
+FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 run to bytes).
 
 Printed: one JSON line with throughput (tokens/s), the roofline of the
 dominant kernel (algorithmic bytes per launch over its mean duration against
@@ -37,7 +43,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn tokens/s + HBM GB/s & MFMA TFLOP/s (% roofline), B=64 L=4096"
 COUNTERS = os.path.join(ROOT, "profiles", "mla_decode_dsv3_b64_l4096_counters.json")
-KERNEL_SRC = os.path.join(ROOT, "latent_kv_decode_amd", "csrc", "decode_mfma.hip")
+KERNEL_SRC = os.path.join(ROOT, "latent_kv_decode_amd", "csrc", "decode_wide.hip")
+COPY_BYTES = 1 << 30
 ROTATE = 4
 
 
@@ -58,6 +65,44 @@ def measured_traffic():
     if c.get("kernel_source_sha") != kernel_sha():
         return None
     return c.get("hbm_bytes_per_launch")
+
+
+class HipEvents:
+    """Raw hipEvent_t handles through the HIP runtime (ctypes): the library
+    records them on its own launch stream around the attention kernel."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+
+    def create(self):
+        e = self.ct.c_void_p()
+        assert self.hip.hipEventCreate(self.ct.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, e0, e1):
+        ms = self.ct.c_float()
+        assert self.hip.hipEventSynchronize(self.ct.c_void_p(e1)) == 0
+        assert self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ct.c_void_p(e0), self.ct.c_void_p(e1)) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(self.ct.c_void_p(e))
+
+
+def calibrate_copy(steps):
+    """A plain 1 GiB device copy, `steps` times: FETCH_SIZE and WRITE_SIZE of
+    this kernel in a rocprofv3 run give the counters' bytes-per-unit scale."""
+    import torch
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "steps": steps}), flush=True)
 
 
 def to_dev(a, torch):
@@ -103,11 +148,16 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the decode path is built and measured on a single MI355X)", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.steps if args.steps != 200 else 5)
+        return
 
     import torch
     import latent_kv_decode_amd as lkv
@@ -132,12 +182,16 @@ def main():
     lse = torch.empty((w.B, w.s_q, w.h_q), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(i):
+    hip = HipEvents()
+    kev = [(hip.create(), hip.create()) for _ in range(args.steps)]
+
+    def step(i, events=None):
         kv = kvs[i % ROTATE]
         lkv.lkv_mla_decode(q_nope, q_rope, kv, kv[w.n_lat * w.d_c:], bt, sl, n_latent=w.n_lat,
                            page_size=w.page_size, softmax_scale=w.scale, causal=w.causal,
                            kv_tok_stride=width, rope_tok_stride=width, num_splits=args.num_splits,
-                           seqlens_host=x["seqlens"], out=out, lse=lse, stream=stream)
+                           seqlens_host=x["seqlens"], out=out, lse=lse, stream=stream,
+                           kernel_events=events)
 
     log(f"[bench] warmup {args.warmup}")
     for i in range(args.warmup):
@@ -150,19 +204,24 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
-        step(i)
+        step(i, kev[i])
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e-3  # seconds
+    kern = np.array([hip.elapsed_ms(a, b) for a, b in kev]) * 1e-3
+    for a, b in kev:
+        hip.destroy(a)
+        hip.destroy(b)
     t_step = float(per.mean())
+    t_kern = float(kern.mean())
     ms_per_step = wall / args.steps * 1e3
 
     work = rf.mla_work(x["seqlens"], s_q=w.s_q, h_q=w.h_q, n_lat=w.n_lat, d_c=w.d_c,
                        d_rope=w.d_rope, page_size=w.page_size, causal=w.causal)
     tokens = w.B * w.s_q
-    hbm = work.bytes / t_step / 1e9
-    tflops = work.flops / t_step / 1e12
+    hbm = work.bytes / t_kern / 1e9
+    tflops = work.flops / t_kern / 1e12
 
     # quick sampled parity check of the timed output against the oracle
     import oracle
@@ -199,8 +258,10 @@ def main():
                      "frac": hbm / rf.MI355X_HBM_GBPS, "traffic": traffic},
         "mfma": {"achieved": tflops, "peak": rf.MI355X_BF16_TFLOPS, "unit": "TFLOP/s",
                  "frac": tflops / rf.MI355X_BF16_TFLOPS},
-        "kernel_us": t_step * 1e6,
-        "kernel_us_p10_p90": [float(np.percentile(per, 10) * 1e6), float(np.percentile(per, 90) * 1e6)],
+        "step_us": t_step * 1e6,
+        "kernel_us": t_kern * 1e6,
+        "kernel_us_p10_p90": [float(np.percentile(kern, 10) * 1e6), float(np.percentile(kern, 90) * 1e6)],
+        "kernel": "mla_wide_kernel (attention); the step adds the split-KV combine",
         "algorithmic": {"bytes_per_launch": work.bytes, "flops_per_launch": work.flops,
                         "intensity": work.intensity},
         "parity_sample_rel_l2": rel,

@@ -119,11 +119,14 @@ const char *lkv_last_error(void);
  *   seqlens_host  host int32 [batch] copy of seqlens, or NULL.  Used only to
  *           skip the combine pass when no sequence is split; it must then
  *           equal the device values.
- * Supported: bf16 with d_c in {64, 128, 256, 512}, d_rope in {0, 16, 32, 64},
- *   (h_q / n_latent) * s_q a multiple of 16 or at most 16... see
- *   LKV_ERR_UNSUPPORTED text; f32 with d_c + d_rope <= 1024.  Any page_size
- *   >= 1.  Pointers 16-byte aligned, strides multiples of 8 elements (bf16)
- *   or 4 (f32).
+ *   kernel_events  optional pair of hipEvent_t (either may be NULL): recorded
+ *           on `stream` immediately before and after the attention kernel
+ *           (not the combine pass), for timing that kernel alone.
+ * Supported: bf16 with (d_c, d_rope) in {(512, 64), (256, 64), (128, 64),
+ *   (512, 0)}, and also (256, 0) when a latent head has more than 32 query
+ *   rows ((h_q / n_latent) * s_q > 32); f32 with d_c + d_rope <= 1024.  Any
+ *   page_size >= 1.  Pointers 16-byte aligned, strides multiples of 8
+ *   elements (bf16) or 4 (f32).
  * ---------------------------------------------------------------------- */
 typedef struct {
   uint32_t struct_size;
@@ -146,6 +149,7 @@ typedef struct {
   void *workspace;
   size_t workspace_bytes;
   void *stream; /* hipStream_t */
+  void *kernel_events[2]; /* hipEvent_t or NULL each */
 } lkv_mla_args;
 
 lkv_status lkv_mla_decode(const lkv_mla_args *args);
@@ -169,9 +173,9 @@ lkv_status lkv_mla_decode_workspace_size(const lkv_mla_args *args, size_t *bytes
  *   v_cache  device, element (p, s, g, d) at (p*page_size + s)*v_tok_stride + g*d_h + d
  *   k_rope   device, as in lkv_mla_args; NULL iff d_rope == 0
  *   out      device [batch, s_q, h_q, d_h];  lse device float32 [batch, s_q, h_q] or NULL
- *   workspace / num_splits / seqlens_host as in lkv_mla_args.
- * Supported: bf16 with d_h in {64, 128, 256}, d_rope in {0, 16, 32, 64}; f32
- *   with d_h + d_rope <= 1024.
+ *   workspace / num_splits / seqlens_host / kernel_events as in lkv_mla_args.
+ * Supported: bf16 with (d_h, d_rope) in {(128, 64), (128, 0), (64, 0),
+ *   (256, 0)}; f32 with d_h + d_rope <= 1024.
  * ---------------------------------------------------------------------- */
 typedef struct {
   uint32_t struct_size;
@@ -196,6 +200,7 @@ typedef struct {
   void *workspace;
   size_t workspace_bytes;
   void *stream;
+  void *kernel_events[2]; /* hipEvent_t or NULL each */
 } lkv_gqa_args;
 
 lkv_status lkv_gqa_decode(const lkv_gqa_args *args);

@@ -45,7 +45,7 @@ class MlaArgs(ctypes.Structure):
                 ("kv_tok_stride", _L), ("k_rope", _V), ("rope_tok_stride", _L),
                 ("block_table", _V), ("seqlens", _V), ("seqlens_host", _V), ("out", _V),
                 ("lse", _V), ("workspace", _V), ("workspace_bytes", ctypes.c_size_t),
-                ("stream", _V)]
+                ("stream", _V), ("kernel_events", _V * 2)]
 
 
 class GqaArgs(ctypes.Structure):
@@ -56,7 +56,7 @@ class GqaArgs(ctypes.Structure):
                 ("k_tok_stride", _L), ("v_cache", _V), ("v_tok_stride", _L), ("k_rope", _V),
                 ("rope_tok_stride", _L), ("block_table", _V), ("seqlens", _V),
                 ("seqlens_host", _V), ("out", _V), ("lse", _V), ("workspace", _V),
-                ("workspace_bytes", ctypes.c_size_t), ("stream", _V)]
+                ("workspace_bytes", ctypes.c_size_t), ("stream", _V), ("kernel_events", _V * 2)]
 
 
 class ExpandArgs(ctypes.Structure):
@@ -173,6 +173,13 @@ def _workspace(device, nbytes: int):
 
 
 # ----------------------------------------------------------- entry points
+def _set_events(a, kernel_events):
+    if kernel_events is not None:
+        e0, e1 = kernel_events
+        a.kernel_events[0] = e0 or None
+        a.kernel_events[1] = e1 or None
+
+
 def _mla_args(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, n_latent, page_size,
               softmax_scale, causal, kv_tok_stride, rope_tok_stride, num_splits):
     B, s_q, h_q, d_c = q_nope.shape
@@ -207,13 +214,14 @@ def lkv_mla_decode_workspace_size(q_nope, q_rope, c_kv, k_rope, block_table, seq
 def lkv_mla_decode(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, *, n_latent=1,
                    page_size, softmax_scale, causal=True, kv_tok_stride=None,
                    rope_tok_stride=None, num_splits=0, seqlens_host=None, out=None, lse=None,
-                   return_lse=True, workspace=None, stream=None):
+                   return_lse=True, workspace=None, stream=None, kernel_events=None):
     """MLA absorbed decode (lkv.h: lkv_mla_decode).  Returns (out, lse).
 
     q_nope [B, s_q, h_q, d_c], q_rope [B, s_q, h_q, d_rope] (or None with
     d_rope = 0); c_kv / k_rope are the paged caches (base pointers; element
     offsets follow kv_tok_stride / rope_tok_stride); block_table int32
-    [B, max_pages]; seqlens int32 [B] on the device.
+    [B, max_pages]; seqlens int32 [B] on the device.  kernel_events: optional
+    pair of raw hipEvent_t handles (ints) recorded around the attention kernel.
     """
     torch = _torch()
     a = _mla_args(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, n_latent, page_size,
@@ -234,6 +242,7 @@ def lkv_mla_decode(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, *, n_late
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.stream = _stream(stream)
+    _set_events(a, kernel_events)
     _check(lib.lkv_mla_decode(ctypes.byref(a)))
     del sh
     return out, lse
@@ -274,9 +283,9 @@ def lkv_gqa_decode_workspace_size(q, q_rope, k_cache, v_cache, k_rope, block_tab
 def lkv_gqa_decode(q, q_rope, k_cache, v_cache, k_rope, block_table, seqlens, *, n_kv, page_size,
                    softmax_scale, causal=True, k_tok_stride=None, v_tok_stride=None,
                    rope_tok_stride=None, num_splits=0, seqlens_host=None, out=None, lse=None,
-                   return_lse=True, workspace=None, stream=None):
+                   return_lse=True, workspace=None, stream=None, kernel_events=None):
     """Grouped-query decode over an expanded cache (lkv.h: lkv_gqa_decode).
-    Returns (out [B, s_q, h_q, d_h], lse)."""
+    Returns (out [B, s_q, h_q, d_h], lse); kernel_events as in lkv_mla_decode."""
     torch = _torch()
     a = _gqa_args(q, q_rope, k_cache, v_cache, k_rope, block_table, seqlens, n_kv, page_size,
                   softmax_scale, causal, k_tok_stride, v_tok_stride, rope_tok_stride, num_splits)
@@ -296,6 +305,7 @@ def lkv_gqa_decode(q, q_rope, k_cache, v_cache, k_rope, block_table, seqlens, *,
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.stream = _stream(stream)
+    _set_events(a, kernel_events)
     _check(lib.lkv_gqa_decode(ctypes.byref(a)))
     del sh
     return out, lse

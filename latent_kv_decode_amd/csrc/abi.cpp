@@ -71,7 +71,8 @@ struct Shape {
 };
 
 struct Plan {
-  int rows;        // ROWS template (bf16 path)
+  int wide_waves;  // > 0: latent path with many rows per work-group (waves per work-group)
+  int rows;        // query rows per work-group (bf16 path)
   int row_tiles;
   int n_chunks;
   size_t ws_opart, ws_lse, ws_meta, ws_total;
@@ -79,7 +80,10 @@ struct Plan {
 
 lkv_status make_plan(const Shape &s, Plan *pl) {
   const int rows_per_kvh = s.s_q * (s.h_q / s.n_kvh);
-  pl->rows = lkv::mfma_decode_rows(rows_per_kvh);
+  // Many query rows over one latent: one work-group takes 64 of them and
+  // reads each cache tile once for all of them.
+  pl->wide_waves = s.dtype == LKV_BF16 && s.v_alias && rows_per_kvh > 32 && lkv::mla_wide_supported(s.dk, s.dr) ? 4 : 0;
+  pl->rows = pl->wide_waves ? lkv::mla_wide_rows(pl->wide_waves) : lkv::mfma_decode_rows(rows_per_kvh);
   pl->row_tiles = (rows_per_kvh + pl->rows - 1) / pl->rows;
   int cus = 0;
   if (device_cus(&cus) != 0) return fail(LKV_ERR_HIP, "cannot query the device compute-unit count");
@@ -122,7 +126,9 @@ lkv_status check_shape(const Shape &s) {
   if ((long long)s.B * s.s_q * s.h_q > (1LL << 30)) return fail(LKV_ERR_SHAPE, "batch * s_q * h_q exceeds 2^30 rows");
   if (s.num_splits < 0) return fail(LKV_ERR_SHAPE, "num_splits %d is negative", s.num_splits);
   if (s.dtype == LKV_BF16) {
-    if (!lkv::mfma_decode_supported(s.dk, s.dr, s.dv, s.v_alias, s.s_q * (s.h_q / s.n_kvh)))
+    const int rows_per_kvh = s.s_q * (s.h_q / s.n_kvh);
+    const bool wide = s.v_alias && rows_per_kvh > 32 && lkv::mla_wide_supported(s.dk, s.dr);
+    if (!wide && !lkv::mfma_decode_supported(s.dk, s.dr, s.dv, s.v_alias, rows_per_kvh))
       return fail(LKV_ERR_UNSUPPORTED,
                   "no bf16 kernel for key width %d + RoPE %d, value width %d (%s); compiled: latent "
                   "512+64, 256+64, 128+64, 512+0; grouped 128+64, 128+0, 64+0, 256+0",
@@ -142,6 +148,7 @@ struct Ptrs {
   void *ws;
   size_t ws_bytes;
   hipStream_t stream;
+  void *const *events;  // [2], entries may be NULL
 };
 
 lkv_status check_ptrs(const Shape &s, const Ptrs &p) {
@@ -212,16 +219,25 @@ lkv_status run_decode(const Shape &s, const Ptrs &p, float scale) {
 
   hipError_t e;
   if (s.dtype == LKV_F32) {
+    if (p.events[0] && (e = hipEventRecord(static_cast<hipEvent_t>(p.events[0]), p.stream)) != hipSuccess)
+      return hip_fail(e, "kernel_events[0] record");
     e = lkv::launch_f32_decode(d, p.stream);
     if (e != hipSuccess) return hip_fail(e, "float32 decode launch");
+    if (p.events[1] && (e = hipEventRecord(static_cast<hipEvent_t>(p.events[1]), p.stream)) != hipSuccess)
+      return hip_fail(e, "kernel_events[1] record");
     return LKV_OK;
   }
   char *ws = static_cast<char *>(p.ws);
   d.o_part = reinterpret_cast<float *>(ws);
   d.lse_part = reinterpret_cast<float *>(ws + pl.ws_opart);
   d.meta = reinterpret_cast<int32_t *>(ws + pl.ws_opart + pl.ws_lse);
-  e = lkv::launch_mfma_decode(d, s.v_alias, pl.rows, p.stream);
+  if (p.events[0] && (e = hipEventRecord(static_cast<hipEvent_t>(p.events[0]), p.stream)) != hipSuccess)
+    return hip_fail(e, "kernel_events[0] record");
+  e = pl.wide_waves ? lkv::launch_mla_wide(d, pl.wide_waves, p.stream)
+                    : lkv::launch_mfma_decode(d, s.v_alias, pl.rows, p.stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (p.events[1] && (e = hipEventRecord(static_cast<hipEvent_t>(p.events[1]), p.stream)) != hipSuccess)
+    return hip_fail(e, "kernel_events[1] record");
   if (p.seqlens_host && !any_split(p.seqlens_host, s.B, pl.n_chunks)) return LKV_OK;
   lkv::CombineParams c{};
   c.o_part = d.o_part;
@@ -279,7 +295,7 @@ lkv_status lkv_mla_decode(const lkv_mla_args *a) {
     return fail(LKV_ERR_SHAPE, "kv_tok_stride %lld < n_latent * d_c", (long long)a->kv_tok_stride);
   Ptrs p{a->q_nope, a->q_rope, a->c_kv, a->k_rope, a->c_kv, a->kv_tok_stride, a->rope_tok_stride,
          a->kv_tok_stride, a->block_table, a->seqlens, a->seqlens_host, a->out, a->lse,
-         a->workspace, a->workspace_bytes, static_cast<hipStream_t>(a->stream)};
+         a->workspace, a->workspace_bytes, static_cast<hipStream_t>(a->stream), a->kernel_events};
   return run_decode(s, p, a->softmax_scale);
 }
 
@@ -302,7 +318,7 @@ lkv_status lkv_gqa_decode(const lkv_gqa_args *a) {
   if (!a->v_cache) return fail(LKV_ERR_NULL, "v_cache is NULL");
   Ptrs p{a->q, a->q_rope, a->k_cache, a->k_rope, a->v_cache, a->k_tok_stride, a->rope_tok_stride,
          a->v_tok_stride, a->block_table, a->seqlens, a->seqlens_host, a->out, a->lse,
-         a->workspace, a->workspace_bytes, static_cast<hipStream_t>(a->stream)};
+         a->workspace, a->workspace_bytes, static_cast<hipStream_t>(a->stream), a->kernel_events};
   return run_decode(s, p, a->softmax_scale);
 }
 

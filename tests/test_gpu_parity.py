@@ -102,6 +102,27 @@ def test_mla_head_shapes(lkv, oracle, h_q, n_lat, d_c):
     assert_close(from_dev(out), ro, from_dev(lse), rl, what=f"mla h_q={h_q} n_lat={n_lat}")
 
 
+@pytest.mark.parametrize("h_q,d_c,d_rope,s_q,splits", [
+    (64, 256, 64, 1, 0), (128, 512, 0, 1, 0), (64, 256, 0, 2, 3), (128, 512, 64, 2, 0),
+    (96, 512, 64, 1, 5)])
+def test_mla_many_rows_widths(lkv, oracle, h_q, d_c, d_rope, s_q, splits):
+    """Latent and RoPE widths (512/256, with and without RoPE) with many query
+    rows per latent head, including a row count that is not a multiple of
+    the rows one work-group takes."""
+    w, x = small_mla(500 + h_q + d_c + d_rope + s_q, B=3, h_q=h_q, d_c=d_c, d_rope=d_rope, s_q=s_q,
+                     seqlens=[s_q + 60, 257, 640])
+    note(f"case mla_many_rows h_q={h_q} d_c={d_c} d_rope={d_rope} s_q={s_q} splits={splits}")
+    d = mla_device_inputs(x, w, torch)
+    out, lse = lkv.lkv_mla_decode(d["q_nope"], d["q_rope"] if d_rope else None, d["c_kv"],
+                                  d["k_rope"] if d_rope else None, d["block_table"], d["seqlens"],
+                                  page_size=w.page_size, softmax_scale=w.scale, causal=w.causal,
+                                  kv_tok_stride=d["kv_tok_stride"],
+                                  rope_tok_stride=d["rope_tok_stride"] if d_rope else None,
+                                  num_splits=splits)
+    ro, rl = oracle_mla(oracle, w, x)
+    assert_close(from_dev(out), ro, from_dev(lse), rl, what=f"mla h_q={h_q} d_c={d_c} d_rope={d_rope}")
+
+
 @pytest.mark.parametrize("page", [16, 32, 128, 48])
 def test_mla_page_sizes(lkv, oracle, page):
     w, x = small_mla(400 + page, B=3, page=page, seqlens=[100, 257, 31])
