@@ -4,34 +4,38 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step is one call of the decode path over one batch of synthetic inputs
-already resident in HBM (for the latent path: the MLA absorbed decode kernel,
-plus the split-KV combine when any sequence is split).  The default workload
-is the DeepSeek-V3-shaped MLA absorbed decode: batch 64, 128 query heads over
-a 512-wide latent plus a 64-wide shared RoPE key, 4096 cache tokens each,
-64-token pages, shuffled block table, bf16 with fp32 accumulation.
+already resident in HBM.  The default workload is the DeepSeek-V3-shaped MLA
+absorbed decode: batch 64, 128 query heads over a 512-wide latent plus a
+64-wide shared RoPE key, 4096 cache tokens each, 64-token pages, shuffled
+block table, bf16 with fp32 accumulation (one step = the attention kernel plus
+the split-KV combine).  Other workloads (lkv_inputs.WORKLOADS):
+  gla2_b128_l8192, ragged_mla_b16_sq1, ragged_mla_b16_sq2   latent path
+  gqa_b128_l8192                                             plain GQA
+  gqla_grouped_b64_l4096_sq2   GQLA grouped path: the latent is expanded into
+                               8 key/value groups once (timed separately, not
+                               part of the step), then grouped decode
 
 Timing: W untimed warm-up steps, then K timed steps bracketed by device
 synchronisation.  HIP events on the stream the library launches on time each
-step (attention kernel + split-KV combine), and a second pair, recorded by the
-library itself around the attention kernel (kernel_events), times that kernel
-alone for the roofline.  Four independent copies of the cache rotate from step
-to step so that the 256 MB Infinity Cache cannot hold the working set.
+step, and a second pair, recorded by the library itself around the attention
+kernel (kernel_events), times that kernel alone for the roofline.  Four
+independent copies of the cache rotate from step to step so that the 256 MB
+Infinity Cache cannot hold the working set.
 
     python bench.py --calibrate-copy
 runs only a plain device-to-device copy of a known size (for scaling the
 FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 run to bytes).
 
 Printed: one JSON line with throughput (tokens/s), the roofline of the
-dominant kernel (algorithmic bytes per launch over its mean duration against
+attention kernel (algorithmic bytes per launch over its mean duration against
 the 8 TB/s HBM peak), the MFMA rate against the 2.5 PFLOP/s bf16 peak, and
-the fp64 CPU oracle timed on this host on the same workload.
+the fp64 CPU oracle timed on this host on a bounded sample of the workload.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -42,27 +46,29 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn tokens/s + HBM GB/s & MFMA TFLOP/s (% roofline), B=64 L=4096"
-COUNTERS = os.path.join(ROOT, "profiles", "mla_decode_dsv3_b64_l4096_counters.json")
-KERNEL_SRC = os.path.join(ROOT, "latent_kv_decode_amd", "csrc", "decode_wide.hip")
-COPY_BYTES = 1 << 30
+PROFILES = os.path.join(ROOT, "profiles")
 ROTATE = 4
+COPY_BYTES = 1 << 30
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def source_sha(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernel source changed since the counters were taken."""
-    if not os.path.exists(COUNTERS):
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 counter summary of this workload, or None when there is none or
+    the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{workload}_counters.json")
+    if not os.path.exists(path):
         return None
-    c = json.load(open(COUNTERS))
-    if c.get("kernel_source_sha") != kernel_sha():
+    c = json.load(open(path))
+    src = os.path.join(ROOT, c.get("kernel_source", ""))
+    if not os.path.isfile(src) or c.get("kernel_source_sha") != source_sha(src):
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -84,7 +90,8 @@ class HipEvents:
     def elapsed_ms(self, e0, e1):
         ms = self.ct.c_float()
         assert self.hip.hipEventSynchronize(self.ct.c_void_p(e1)) == 0
-        assert self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ct.c_void_p(e0), self.ct.c_void_p(e1)) == 0
+        assert self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ct.c_void_p(e0),
+                                            self.ct.c_void_p(e1)) == 0
         return ms.value
 
     def destroy(self, e):
@@ -111,32 +118,226 @@ def to_dev(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def cpu_baseline(w, x, budget_s: float):
-    """The fp64 oracle, as it stands, on this host's cores: whole query
-    tokens (all heads of a sequence) until about `budget_s` seconds of CPU
-    work or the whole batch."""
-    import oracle
-    per_seq = w.s_q * w.h_q
-    width = w.n_lat * w.d_c + w.d_rope
-    kv = x["kv"].reshape(-1)
-    done_seqs, elapsed = 0, 0.0
-    chunk = 1
-    while done_seqs < w.B and elapsed < budget_s:
-        n = min(chunk, w.B - done_seqs)
-        rows = np.arange(done_seqs * per_seq, (done_seqs + n) * per_seq, dtype=np.int32)
+def f64(bits):
+    import lkv_inputs as li
+    return li.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def timed_oracle(run_seqs, B: int, budget_s: float):
+    """Call run_seqs(s0, n) on growing groups of whole sequences until about
+    budget_s seconds of oracle time or the whole batch; returns
+    (sequences done, seconds)."""
+    done, elapsed, chunk = 0, 0.0, 1
+    while done < B and elapsed < budget_s:
+        n = min(chunk, B - done)
         t0 = time.perf_counter()
-        oracle.mla_decode(x["q_nope"], x["q_rope"], kv, kv[w.n_lat * w.d_c:], x["block_table"],
-                          x["seqlens"], n_lat=w.n_lat, d_c=w.d_c, d_rope=w.d_rope,
-                          page_size=w.page_size, scale=w.scale, causal=w.causal,
-                          kv_tok_stride=width, rope_tok_stride=width, rows=rows)
+        run_seqs(done, n)
         elapsed += time.perf_counter() - t0
-        done_seqs += n
+        done += n
         chunk = min(chunk * 2, 16)
-    tokens = done_seqs * w.s_q
-    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{done_seqs} of {w.B} sequences (all {w.h_q} heads, {w.s_q} query token(s) "
-                      f"each, full cache length) of the timed workload; {elapsed:.1f} s"}
+    return done, elapsed
+
+
+def rel_l2(got, ref):
+    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+
+# ----------------------------------------------------------------- workloads
+def setup_mla(w, x, args, torch, lkv, rf):
+    import oracle
+    import lkv_inputs as li
+    width = w.n_lat * w.d_c + w.d_rope
+    kvs = [to_dev(x["kv"], torch).reshape(-1)]
+    for _ in range(ROTATE - 1):
+        kvs.append(kvs[0].clone())
+    q_nope, q_rope = to_dev(x["q_nope"], torch), to_dev(x["q_rope"], torch)
+    bt = torch.from_numpy(x["block_table"]).cuda()
+    sl = torch.from_numpy(x["seqlens"]).cuda()
+    out = torch.empty((w.B, w.s_q, w.h_q, w.d_c), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.s_q, w.h_q), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        kv = kvs[i % ROTATE]
+        lkv.lkv_mla_decode(q_nope, q_rope, kv, kv[w.n_lat * w.d_c:], bt, sl, n_latent=w.n_lat,
+                           page_size=w.page_size, softmax_scale=w.scale, causal=w.causal,
+                           kv_tok_stride=width, rope_tok_stride=width, num_splits=args.num_splits,
+                           seqlens_host=x["seqlens"], out=out, lse=lse, stream=stream,
+                           kernel_events=events)
+
+    def oracle_rows(rows):
+        kv0 = x["kv"].reshape(-1)
+        return oracle.mla_decode(x["q_nope"], x["q_rope"], kv0, kv0[w.n_lat * w.d_c:],
+                                 x["block_table"], x["seqlens"], n_lat=w.n_lat, d_c=w.d_c,
+                                 d_rope=w.d_rope, page_size=w.page_size, scale=w.scale,
+                                 causal=w.causal, kv_tok_stride=width, rope_tok_stride=width,
+                                 rows=rows)
+
+    def parity():
+        rows = li.sample_rows(5, w.B, w.s_q, w.h_q, 8)
+        ro, _ = oracle_rows(rows)
+        got = out.float().cpu().numpy().reshape(-1, w.d_c)[rows]
+        return rel_l2(got, ro.reshape(-1, w.d_c)[rows])
+
+    def cpu(budget):
+        per = w.s_q * w.h_q
+        done, el = timed_oracle(
+            lambda s0, n: oracle_rows(np.arange(s0 * per, (s0 + n) * per, dtype=np.int32)),
+            w.B, budget)
+        return done, el, f"{done} of {w.B} sequences (all {w.h_q} heads, {w.s_q} query token(s) " \
+                         f"each, full cache length) of the timed workload"
+
+    work = rf.mla_work(x["seqlens"], s_q=w.s_q, h_q=w.h_q, n_lat=w.n_lat, d_c=w.d_c,
+                       d_rope=w.d_rope, page_size=w.page_size, causal=w.causal)
+    wide = w.h_q // w.n_lat * w.s_q > 32 and w.d_c in (256, 512)
+    return dict(step=step, work=work, parity=parity, cpu=cpu,
+                kernel="mla_wide_kernel" if wide else "mfma_decode_kernel",
+                config={"n_latent": w.n_lat, "d_c": w.d_c, "d_rope": w.d_rope})
+
+
+def setup_gqa(w, x, args, torch, lkv, rf):
+    import oracle
+    import lkv_inputs as li
+    ks = [to_dev(x["k_cache"], torch)]
+    vs = [to_dev(x["v_cache"], torch)]
+    for _ in range(ROTATE - 1):
+        ks.append(ks[0].clone())
+        vs.append(vs[0].clone())
+    q = to_dev(x["q"], torch)
+    bt = torch.from_numpy(x["block_table"]).cuda()
+    sl = torch.from_numpy(x["seqlens"]).cuda()
+    out = torch.empty((w.B, w.s_q, w.h_q, w.d_h), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.s_q, w.h_q), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        lkv.lkv_gqa_decode(q, None, ks[i % ROTATE], vs[i % ROTATE], None, bt, sl, n_kv=w.n_kv,
+                           page_size=w.page_size, softmax_scale=w.scale, causal=w.causal,
+                           num_splits=args.num_splits, seqlens_host=x["seqlens"], out=out,
+                           lse=lse, stream=stream, kernel_events=events)
+
+    def oracle_rows(rows):
+        return oracle.gqa_decode(x["q"], x["k_cache"], x["v_cache"], x["block_table"],
+                                 x["seqlens"], n_kv=w.n_kv, d_h=w.d_h, page_size=w.page_size,
+                                 scale=w.scale, causal=w.causal, rows=rows)
+
+    def parity():
+        rows = li.sample_rows(5, w.B, w.s_q, w.h_q, 8)
+        ro, _ = oracle_rows(rows)
+        got = out.float().cpu().numpy().reshape(-1, w.d_h)[rows]
+        return rel_l2(got, ro.reshape(-1, w.d_h)[rows])
+
+    def cpu(budget):
+        per = w.s_q * w.h_q
+        done, el = timed_oracle(
+            lambda s0, n: oracle_rows(np.arange(s0 * per, (s0 + n) * per, dtype=np.int32)),
+            w.B, budget)
+        return done, el, f"{done} of {w.B} sequences (all {w.h_q} heads) of the timed workload"
+
+    work = rf.gqa_work(x["seqlens"], s_q=w.s_q, h_q=w.h_q, n_kv=w.n_kv, d_h=w.d_h, d_rope=0,
+                       page_size=w.page_size, causal=w.causal)
+    return dict(step=step, work=work, parity=parity, cpu=cpu, kernel="mfma_decode_kernel",
+                config={"n_kv": w.n_kv, "d_h": w.d_h, "d_rope": 0})
+
+
+def setup_gqla(w, x, args, torch, lkv, rf):
+    """GQLA grouped path: expand the latent once (timed on its own), then
+    grouped decode over the expanded K/V plus the latent cache's RoPE part."""
+    import oracle
+    width = w.d_c + w.d_rope
+    kv = to_dev(x["kv"], torch)
+    num_pages, P = kv.shape[0], kv.shape[1]
+    flat = kv.reshape(-1)
+    wuk, wuv = to_dev(x["w_uk"], torch), to_dev(x["w_uv"], torch)
+    bt = torch.from_numpy(x["block_table"]).cuda()
+    sl = torch.from_numpy(x["seqlens"]).cuda()
+    k0 = torch.empty((num_pages, P, w.n_kv, w.d_h), dtype=torch.bfloat16, device="cuda")
+    v0 = torch.empty_like(k0)
+    stream = torch.cuda.current_stream()
+
+    def expand(k_out, v_out):
+        lkv.lkv_gqla_expand_latent(flat, wuk, wuv, bt, sl, k_out, v_out, page_size=w.page_size,
+                                   kv_tok_stride=width, stream=stream)
+
+    for _ in range(2):
+        expand(k0, v0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_exp = 5
+    e0.record(stream)
+    for _ in range(n_exp):
+        expand(k0, v0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_exp = e0.elapsed_time(e1) * 1e-3 / n_exp
+    ks, vs = [k0], [v0]
+    for _ in range(ROTATE - 1):
+        ks.append(k0.clone())
+        vs.append(v0.clone())
+    q, q_rope = to_dev(x["q_nope_h"], torch), to_dev(x["q_rope"], torch)
+    out = torch.empty((w.B, w.s_q, w.h_q, w.d_h), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.s_q, w.h_q), dtype=torch.float32, device="cuda")
+
+    def step(i, events=None):
+        lkv.lkv_gqa_decode(q, q_rope, ks[i % ROTATE], vs[i % ROTATE], flat[w.d_c:], bt, sl,
+                           n_kv=w.n_kv, page_size=w.page_size, softmax_scale=w.scale,
+                           causal=w.causal, rope_tok_stride=width, num_splits=args.num_splits,
+                           seqlens_host=x["seqlens"], out=out, lse=lse, stream=stream,
+                           kernel_events=events)
+
+    def oracle_seqs(seqs, rows):
+        """fp64 expansion of just the tokens of sequences `seqs` (their pages
+        copied into a compact pool), then grouped decode of `rows` (flat row
+        ids within that compact batch)."""
+        pages = [x["block_table"][s, : (int(x["seqlens"][s]) + P - 1) // P] for s in seqs]
+        sub_bt = np.full((len(seqs), x["block_table"].shape[1]), -1, np.int32)
+        pool = []
+        for i, pg in enumerate(pages):
+            sub_bt[i, : len(pg)] = np.arange(len(pool), len(pool) + len(pg))
+            pool.extend(pg.tolist())
+        sub_kv = x["kv"][np.array(pool)]
+        sub_sl = x["seqlens"][seqs]
+        rk, rv = oracle.expand_latent(sub_kv.reshape(-1), f64(x["w_uk"]), f64(x["w_uv"]), sub_bt,
+                                      sub_sl, page_size=P, num_pages=len(pool),
+                                      kv_tok_stride=width)
+        return oracle.gqa_decode(f64(x["q_nope_h"])[seqs], np.nan_to_num(rk), np.nan_to_num(rv),
+                                 sub_bt, sub_sl, n_kv=w.n_kv, d_h=w.d_h, page_size=P,
+                                 scale=w.scale, causal=w.causal, q_rope=f64(x["q_rope"])[seqs],
+                                 k_rope=np.nan_to_num(f64(sub_kv[..., w.d_c:])), d_rope=w.d_rope,
+                                 rows=rows)
+
+    def parity():
+        per = w.s_q * w.h_q
+        seqs = [0, w.B - 1]
+        rng = np.random.default_rng(13)
+        sub_rows = np.sort(np.concatenate(
+            [i * per + rng.choice(per, 8, replace=False) for i in range(len(seqs))])).astype(np.int32)
+        rows = np.array([seqs[int(r) // per] * per + int(r) % per for r in sub_rows])
+        ro, _ = oracle_seqs(seqs, sub_rows)
+        got = out.float().cpu().numpy().reshape(-1, w.d_h)[rows]
+        return rel_l2(got, ro.reshape(-1, w.d_h)[sub_rows])
+
+    def cpu(budget):
+        per = w.s_q * w.h_q
+        done, el = timed_oracle(
+            lambda s0, n: oracle_seqs(list(range(s0, s0 + n)), np.arange(n * per, dtype=np.int32)),
+            w.B, budget)
+        return done, el, f"{done} of {w.B} sequences: fp64 latent expansion of their tokens " \
+                         f"plus grouped decode of all {w.h_q} heads x {w.s_q} query tokens"
+
+    work = rf.gqa_work(x["seqlens"], s_q=w.s_q, h_q=w.h_q, n_kv=w.n_kv, d_h=w.d_h,
+                       d_rope=w.d_rope, page_size=w.page_size, causal=w.causal)
+    n_tok = int(np.sum(x["seqlens"]))
+    ew = rf.expand_work(n_tok, g=w.n_kv, d_c=w.d_c, d_h=w.d_h)
+    extra = {"expansion": {"us": t_exp * 1e6, "tokens": n_tok, "algorithmic_bytes": ew.bytes,
+                           "flops": ew.flops, "GB_per_s": ew.bytes / t_exp / 1e9,
+                           "TFLOP_per_s": ew.flops / t_exp / 1e12,
+                           "note": "cache-write-time expansion, not part of the timed step"}}
+    return dict(step=step, work=work, parity=parity, cpu=cpu, kernel="mfma_decode_kernel",
+                extra=extra, config={"g": w.n_kv, "d_h": w.d_h, "d_rope": w.d_rope, "d_c": w.d_c})
+
+
+SETUPS = {"mla": setup_mla, "gqa": setup_gqa, "gqla": setup_gqla}
 
 
 def main():
@@ -166,33 +367,17 @@ def main():
 
     lkv.load_library()
     w = li.workload(args.workload)
-    if w.kind != "mla":
-        print("bench.py times the latent (MLA / GLA) workloads", file=sys.stderr)
+    if w.dtype != "bf16":
+        print("bench.py times the bf16 workloads", file=sys.stderr)
         sys.exit(2)
     log(f"[bench] generating {w.name}")
     x = li.generate(w)
-    width = w.n_lat * w.d_c + w.d_rope
-    kvs = [to_dev(x["kv"], torch).reshape(-1)]
-    for _ in range(ROTATE - 1):
-        kvs.append(kvs[0].clone())
-    q_nope, q_rope = to_dev(x["q_nope"], torch), to_dev(x["q_rope"], torch)
-    bt = torch.from_numpy(x["block_table"]).cuda()
-    sl = torch.from_numpy(x["seqlens"]).cuda()
-    out = torch.empty((w.B, w.s_q, w.h_q, w.d_c), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((w.B, w.s_q, w.h_q), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
+    s = SETUPS[w.kind](w, x, args, torch, lkv, rf)
+    step, work = s["step"], s["work"]
 
     hip = HipEvents()
     kev = [(hip.create(), hip.create()) for _ in range(args.steps)]
-
-    def step(i, events=None):
-        kv = kvs[i % ROTATE]
-        lkv.lkv_mla_decode(q_nope, q_rope, kv, kv[w.n_lat * w.d_c:], bt, sl, n_latent=w.n_lat,
-                           page_size=w.page_size, softmax_scale=w.scale, causal=w.causal,
-                           kv_tok_stride=width, rope_tok_stride=width, num_splits=args.num_splits,
-                           seqlens_host=x["seqlens"], out=out, lse=lse, stream=stream,
-                           kernel_events=events)
-
+    stream = torch.cuda.current_stream()
     log(f"[bench] warmup {args.warmup}")
     for i in range(args.warmup):
         step(i)
@@ -208,35 +393,19 @@ def main():
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e-3  # seconds
+    per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)]) * 1e-3  # seconds
     kern = np.array([hip.elapsed_ms(a, b) for a, b in kev]) * 1e-3
     for a, b in kev:
         hip.destroy(a)
         hip.destroy(b)
     t_step = float(per.mean())
     t_kern = float(kern.mean())
-    ms_per_step = wall / args.steps * 1e3
 
-    work = rf.mla_work(x["seqlens"], s_q=w.s_q, h_q=w.h_q, n_lat=w.n_lat, d_c=w.d_c,
-                       d_rope=w.d_rope, page_size=w.page_size, causal=w.causal)
     tokens = w.B * w.s_q
     hbm = work.bytes / t_kern / 1e9
     tflops = work.flops / t_kern / 1e12
-
-    # quick sampled parity check of the timed output against the oracle
-    import oracle
-    rows = li.sample_rows(5, w.B, w.s_q, w.h_q, 8)
-    kv0 = x["kv"].reshape(-1)
-    ro, _ = oracle.mla_decode(x["q_nope"], x["q_rope"], kv0, kv0[w.n_lat * w.d_c:],
-                              x["block_table"], x["seqlens"], n_lat=w.n_lat, d_c=w.d_c,
-                              d_rope=w.d_rope, page_size=w.page_size, scale=w.scale,
-                              causal=w.causal, kv_tok_stride=width, rope_tok_stride=width,
-                              rows=rows)
-    got = out.float().cpu().numpy().reshape(-1, w.d_c)[rows]
-    ref = ro.reshape(-1, w.d_c)[rows]
-    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
-
-    traffic = measured_traffic() if args.workload == "dsv3_mla_b64_l4096" else None
+    log("[bench] parity sample against the oracle")
+    rel = s["parity"]()
     result = {
         "metric": METRIC,
         "value": tokens / t_step,
@@ -244,31 +413,41 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "seq_len": int(x["seqlens"].max()),
-                   "s_q": w.s_q, "h_q": w.h_q, "n_latent": w.n_lat, "d_c": w.d_c,
-                   "d_rope": w.d_rope, "page_size": w.page_size, "table": w.table,
+                   "total_cache_tokens": int(np.sum(x["seqlens"])), "s_q": w.s_q, "h_q": w.h_q,
+                   **s["config"], "page_size": w.page_size, "table": w.table,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": hbm, "peak": rf.MI355X_HBM_GBPS, "unit": "GB/s",
-                     "frac": hbm / rf.MI355X_HBM_GBPS, "traffic": traffic},
+                     "frac": hbm / rf.MI355X_HBM_GBPS, "traffic": measured_traffic(w.name)},
         "mfma": {"achieved": tflops, "peak": rf.MI355X_BF16_TFLOPS, "unit": "TFLOP/s",
                  "frac": tflops / rf.MI355X_BF16_TFLOPS},
-        "step_us": t_step * 1e6,
+        "kernel": f"{s['kernel']} (attention, timed alone); a step adds the split-KV combine "
+                  "when a sequence spans several shares",
         "kernel_us": t_kern * 1e6,
-        "kernel_us_p10_p90": [float(np.percentile(kern, 10) * 1e6), float(np.percentile(kern, 90) * 1e6)],
-        "kernel": "mla_wide_kernel (attention); the step adds the split-KV combine",
+        "kernel_us_median_p10_p90": [float(np.median(kern) * 1e6),
+                                     float(np.percentile(kern, 10) * 1e6),
+                                     float(np.percentile(kern, 90) * 1e6)],
+        "step_us": t_step * 1e6,
+        "step_us_median_p10_p90": [float(np.median(per) * 1e6), float(np.percentile(per, 10) * 1e6),
+                                   float(np.percentile(per, 90) * 1e6)],
         "algorithmic": {"bytes_per_launch": work.bytes, "flops_per_launch": work.flops,
                         "intensity": work.intensity},
         "parity_sample_rel_l2": rel,
     }
+    result.update(s.get("extra", {}))
     if not args.no_cpu_baseline:
+        import oracle
         log("[bench] cpu baseline (fp64 oracle)")
-        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+        done, el, sample = s["cpu"](args.cpu_budget)
+        result["cpu_baseline"] = {"value": done * w.s_q / el, "unit": "tokens/s",
+                                  "cores": oracle.num_threads(), "kind": "oracle",
+                                  "sample": f"{sample}; {el:.1f} s"}
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
