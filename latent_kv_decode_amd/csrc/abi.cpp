@@ -70,8 +70,12 @@ struct Shape {
   bool v_alias;
 };
 
+// Kernels for many query rows over one latent head: score and value products
+// on separate waves (split) or on the same waves (wide).
+enum { kLatentNone = 0, kLatentWide = 1, kLatentSplit = 2 };
+
 struct Plan {
-  int wide_waves;  // > 0: latent path with many rows per work-group (waves per work-group)
+  int latent;      // kernel for many rows over one latent (0: the row-tiled kernel)
   int rows;        // query rows per work-group (bf16 path)
   int row_tiles;
   int n_chunks;
@@ -82,8 +86,12 @@ lkv_status make_plan(const Shape &s, Plan *pl) {
   const int rows_per_kvh = s.s_q * (s.h_q / s.n_kvh);
   // Many query rows over one latent: one work-group takes 64 of them and
   // reads each cache tile once for all of them.
-  pl->wide_waves = s.dtype == LKV_BF16 && s.v_alias && rows_per_kvh > 32 && lkv::mla_wide_supported(s.dk, s.dr) ? 4 : 0;
-  pl->rows = pl->wide_waves ? lkv::mla_wide_rows(pl->wide_waves) : lkv::mfma_decode_rows(rows_per_kvh);
+  pl->latent = kLatentNone;
+  if (s.dtype == LKV_BF16 && s.v_alias && rows_per_kvh > 32 && lkv::mla_split_supported(s.dk, s.dr))
+    pl->latent = kLatentSplit;
+  pl->rows = pl->latent == kLatentSplit  ? lkv::mla_split_rows()
+             : pl->latent == kLatentWide ? lkv::mla_wide_rows(1)
+                                         : lkv::mfma_decode_rows(rows_per_kvh);
   pl->row_tiles = (rows_per_kvh + pl->rows - 1) / pl->rows;
   int cus = 0;
   if (device_cus(&cus) != 0) return fail(LKV_ERR_HIP, "cannot query the device compute-unit count");
@@ -127,7 +135,7 @@ lkv_status check_shape(const Shape &s) {
   if (s.num_splits < 0) return fail(LKV_ERR_SHAPE, "num_splits %d is negative", s.num_splits);
   if (s.dtype == LKV_BF16) {
     const int rows_per_kvh = s.s_q * (s.h_q / s.n_kvh);
-    const bool wide = s.v_alias && rows_per_kvh > 32 && lkv::mla_wide_supported(s.dk, s.dr);
+    const bool wide = s.v_alias && rows_per_kvh > 32 && lkv::mla_split_supported(s.dk, s.dr);
     if (!wide && !lkv::mfma_decode_supported(s.dk, s.dr, s.dv, s.v_alias, rows_per_kvh))
       return fail(LKV_ERR_UNSUPPORTED,
                   "no bf16 kernel for key width %d + RoPE %d, value width %d (%s); compiled: latent "
@@ -166,6 +174,9 @@ lkv_status check_ptrs(const Shape &s, const Ptrs &p) {
       if (x && !aligned16(x)) return fail(LKV_ERR_ALIGN, "bf16 buffers must be 16-byte aligned");
     if (p.k_stride % 8 || p.v_stride % 8 || (s.dr > 0 && p.r_stride % 8))
       return fail(LKV_ERR_ALIGN, "bf16 token strides must be multiples of 8 elements");
+    // tile loads address 64 token rows from one base with 32-bit offsets
+    if (p.k_stride > (1 << 24) || p.v_stride > (1 << 24) || p.r_stride > (1 << 24))
+      return fail(LKV_ERR_SHAPE, "bf16 token strides above 2^24 elements are not supported");
     if (!p.ws) return fail(LKV_ERR_WORKSPACE, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(p.ws) & 255) return fail(LKV_ERR_ALIGN, "workspace must be 256-byte aligned");
   } else {
@@ -233,8 +244,9 @@ lkv_status run_decode(const Shape &s, const Ptrs &p, float scale) {
   d.meta = reinterpret_cast<int32_t *>(ws + pl.ws_opart + pl.ws_lse);
   if (p.events[0] && (e = hipEventRecord(static_cast<hipEvent_t>(p.events[0]), p.stream)) != hipSuccess)
     return hip_fail(e, "kernel_events[0] record");
-  e = pl.wide_waves ? lkv::launch_mla_wide(d, pl.wide_waves, p.stream)
-                    : lkv::launch_mfma_decode(d, s.v_alias, pl.rows, p.stream);
+  e = pl.latent == kLatentSplit  ? lkv::launch_mla_split(d, p.stream)
+      : pl.latent == kLatentWide ? lkv::launch_mla_wide(d, 1, p.stream)
+                                 : lkv::launch_mfma_decode(d, s.v_alias, pl.rows, p.stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (p.events[1] && (e = hipEventRecord(static_cast<hipEvent_t>(p.events[1]), p.stream)) != hipSuccess)
     return hip_fail(e, "kernel_events[1] record");

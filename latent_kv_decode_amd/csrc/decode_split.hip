@@ -1,0 +1,603 @@
+// decode_split.hip -- MLA absorbed decode with the score and value products
+// on different waves [GQLA explainer, technical summary section 2,
+// MQA-absorbed path: every query head reads the one shared latent c_KV plus
+// the shared RoPE key, and the latent is also the value].
+//
+// A work-group takes 64 query rows of one latent head and a share of the
+// batch's cache tiles.  Its eight waves split the work by stage:
+//   waves 0..3  (score waves) hold the query of 16 rows each in registers and
+//               compute S^T = K Q^T per 32-token tile, the online softmax
+//               (running maximum, row sums) and P = exp(S - m) in bf16;
+//   waves 4..7  (value waves) hold the output accumulator (fp32, transposed)
+//               of 32 rows x half of the value columns each and compute
+//               O^T += V^T P^T.
+// P (already in the MFMA operand layout) and the per-row rescale factors go
+// from score to value waves through LDS, one tile behind: in iteration k the
+// score waves work on tile k while the value waves work on tile k - 1, and
+// one barrier per tile hands P over.  Each SIMD runs one score and one value
+// wave, so the softmax of one overlaps the MFMAs of the other, and each value
+// fragment read from LDS feeds two MFMAs (two 16-row blocks).  Tiles (32
+// tokens) are staged by direct-to-LDS buffer loads into a ring of four
+// buffers, two tiles ahead of the score waves.
+#include <type_traits>
+
+#include "lkv_internal.h"
+
+namespace lkv {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+typedef __bf16 bf16;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kT = 32;     // tokens per tile
+constexpr int kRing = 4;   // tile buffers
+constexpr int kRows = 64;  // query rows per work-group
+constexpr float kLn2 = 0.693147180559945309f;
+// The softmax reference maximum moves only when a tile's maximum exceeds it
+// by more than this (base-2 units); probabilities stay below 2^kLazy.
+constexpr float kLazy = 8.0f;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// LDS swizzle (128 banks of 4 bytes; a 16-byte read is served 32 lanes at a
+// time, a transposing 8-byte read 64 lanes at a time).  Chunk c (16 bytes)
+// of row r of a region with CPR chunks per row sits at slot swz<CPR>(c, r):
+//   CPR >= 32: c ^ 2*(r mod 16) -- a key read (16 rows x 2 adjacent chunks)
+//              and a value transpose read (16 rows x one chunk pair) both
+//              cover 32 distinct slots of a 512-byte window;
+//   CPR == 8:  c ^ ((r / 2) mod 8) for 128-byte RoPE rows.
+template <int CPR>
+__device__ __forceinline__ int swz(int c, int r) {
+  static_assert(CPR == 8 || CPR == 32 || CPR == 64, "region row length");
+  if constexpr (CPR >= 32) return c ^ ((r & 15) << 1);
+  else return c ^ ((r >> 1) & 7);
+}
+
+__device__ __forceinline__ s16x4 lds_read_tr(const bf16 *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+}
+__device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// s_waitcnt vmcnt(N): at most N vector memory loads of this wave in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Reductions over the four 16-lane groups (partners l ^ 16 and l ^ 32).
+__device__ __forceinline__ float xlane_max16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xlane_max32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xlane_sum16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xlane_sum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Share plan over 64-token units (the row-tiled kernel's definition): the
+// concatenated units of all sequences (an empty sequence counts one) cut into
+// n_chunks shares of ceil(total / n_chunks) units.
+__device__ __forceinline__ int seq_units(int L) { return L <= 0 ? 1 : (L + kTile - 1) / kTile; }
+
+__device__ bool plan_share(const int32_t *seqlens, int B, int C, int c, int *sh, int &chunk, int &t0,
+                           int &t1, int &b0, int &cu0) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int per = (B + kThreads - 1) / kThreads;
+  const int s0 = min(B, tid * per), s1 = min(B, s0 + per);
+  int local = 0;
+  for (int b = s0; b < s1; ++b) local += seq_units(seqlens[b]);
+  int v = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) sh[w] = v;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const int s = sh[i];
+    if (i < w) before += s;
+    total += s;
+  }
+  const int excl = before + v - local;
+  chunk = (total + C - 1) / C;
+  t0 = c * chunk;
+  t1 = min(total, t0 + chunk);
+  __syncthreads();
+  if (t0 >= total) return false;
+  if (t0 >= excl && t0 < excl + local) {
+    int cu = excl;
+    for (int b = s0; b < s1; ++b) {
+      const int nb = seq_units(seqlens[b]);
+      if (t0 < cu + nb) {
+        sh[kWaves] = b;
+        sh[kWaves + 1] = cu;
+        break;
+      }
+      cu += nb;
+    }
+  }
+  __syncthreads();
+  b0 = sh[kWaves];
+  cu0 = sh[kWaves + 1];
+  return true;
+}
+
+__device__ __forceinline__ const char *uniform_ptr(const char *p) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(v));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(v >> 32));
+  return reinterpret_cast<const char *>((static_cast<unsigned long long>(hi) << 32) | lo);
+}
+
+// Direct-to-LDS loads through raw buffer resources (buffer_load ... lds): with
+// this MUBUF form the compiler keeps its waits on LDS reads exact while such
+// loads are in flight.  Dword 3: 32-bit data format, no swizzle, no tid add.
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(uniform_ptr(base)), (short)0, 0x7fffffff,
+                                           kRsrcWord3);
+}
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, bf16 *dst, unsigned voff, unsigned soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
+}
+
+template <int DK, int DR>
+struct SCfg {
+  static_assert((DK == 512 || DK == 256) && (DR == 0 || DR == 64), "widths");
+  static constexpr int KS = (DK + DR) / 32;   // QK^T k-steps
+  static constexpr int KSN = DK / 32;         // of which on the latent
+  static constexpr int MT = DK / 16;          // value column tiles
+  static constexpr int MTH = MT / 2;          // per value wave (half of the columns)
+  static constexpr int CPT = DK / 8;          // 16-byte chunks per latent row
+  static constexpr int ROFF = kT * DK;        // RoPE region of a tile buffer
+  static constexpr int BUF = kT * (DK + DR);  // elements per tile buffer
+  static constexpr int NL = kT / kWaves;      // latent rows staged per wave and tile
+  // RoPE: 8 tokens per score wave and tile, one instruction when the tile is
+  // on one page (eight otherwise; waiting for NIS then waits for more)
+  static constexpr int NIS = NL + (DR > 0 ? 1 : 0);  // tile-load instructions, score wave
+  static constexpr int NIV = NL;                     // tile-load instructions, value wave
+  static constexpr int PX = 2 * 4 * 64 * 8;          // P^T exchange [parity][block][lane] 16 B
+  static constexpr int LDS_BYTES = (kRing * BUF + PX) * 2 + 2 * 64 * 4 + 2 * 4 * 4 + 64 * 4 + 64;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <int DK, int DR>
+__global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodeParams p) {
+  using C = SCfg<DK, DR>;
+  constexpr int KS = C::KS, KSN = C::KSN, MTH = C::MTH, CPT = C::CPT, NL = C::NL;
+  // tile ring as distinct LDS objects (loads into one are provably
+  // independent of reads of the others)
+  __shared__ __attribute__((aligned(16))) bf16 s_b0[C::BUF];
+  __shared__ __attribute__((aligned(16))) bf16 s_b1[C::BUF];
+  __shared__ __attribute__((aligned(16))) bf16 s_b2[C::BUF];
+  __shared__ __attribute__((aligned(16))) bf16 s_b3[C::BUF];
+  __shared__ __attribute__((aligned(16))) bf16 s_px[C::PX];  // P^T fragments
+  __shared__ float s_alpha[2][64];                           // [parity][row]
+  __shared__ int s_moved[2][4];                              // [parity][16-row block]
+  __shared__ float s_fin[64];                                // row sums
+  int *const s_plan = reinterpret_cast<int *>(s_b3);         // free until the first loads
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+
+  // block -> (share, row tile); the row tiles of one share sit on one XCD
+  const int G = p.n_kvh * p.row_tiles;
+  const int bx = blockIdx.x;
+  const int q8 = bx >> 3;
+  const int grp = q8 % G;
+  const int c = (q8 / G) * 8 + (bx & 7);
+  if (c >= p.n_chunks) return;
+  const int kvh = grp / p.row_tiles, rt = grp % p.row_tiles;
+
+  int chunk, u0, u1, b0, cu0;
+  if (!plan_share(p.seqlens, p.B, p.n_chunks, c, s_plan, chunk, u0, u1, b0, cu0)) return;
+
+  const bf16 *__restrict__ qn = static_cast<const bf16 *>(p.q);
+  const bf16 *__restrict__ qr_ = static_cast<const bf16 *>(p.q_rope);
+  const char *kcb = reinterpret_cast<const char *>(static_cast<const bf16 *>(p.k) + (long long)kvh * DK);
+  const char *rcb = static_cast<const char *>(p.r);
+  const long long kstr = p.k_stride * 2, rstr = p.r_stride * 2;
+  const bool aligned_pages = p.page_shift >= 5;
+
+  // The two roles run the same loop (same tiles, same barriers); each is
+  // compiled on its own so that only its own state is live.
+  auto run = [&](auto role_tag) __attribute__((always_inline)) {
+    constexpr bool kScore = decltype(role_tag)::value;
+    constexpr int NI = kScore ? C::NIS : C::NIV;  // this wave's loads per tile
+    // score wave sw: rows 16 sw..; value wave vw: rows 32 (vw & 1).. (blocks
+    // 2 (vw & 1) + nt), value columns 16 MTH (vw >> 1)..
+    const int sw = wu, vw = wu - 4;
+    const int rg = vw & 1, dh = vw >> 1;
+
+    // ---- per-lane LDS offsets (elements) of this role's fragment reads
+    //  score: key A operand (token block tt): row 16tt + n, chunk 4ks + g
+    int koff[kScore ? 8 : 1], roff[2];
+    if constexpr (kScore) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) koff[e] = n * DK + swz<CPT>(4 * e + g, n) * 8;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) roff[e] = DR > 0 ? n * DR + swz<8>(4 * e + g, n) * 8 : 0;
+    }
+    //  value: transpose read of global column tile mt = MTH dh + ml: lane
+    //  (g, n) reads row 4g + n/4 (and the same 16 rows on) at columns
+    //  16mt + 4(n%4)..+3; the slot depends on mt mod 16, plus 32 chunks per
+    //  16 tiles
+    constexpr int NV = MTH < 16 ? MTH : 16;
+    int voff[kScore ? 1 : NV];
+    if constexpr (!kScore) {
+      const int rv = 4 * g + (n >> 2);
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+        voff[j] = rv * DK + swz<CPT>(2 * (MTH * dh + j) + ((n & 3) >> 1), rv) * 8 + 4 * (n & 1);
+    }
+    // tile loads: wave w stages tile rows w and w + 8, ... (one latent row
+    // per instruction; lane l fetches chunk swz(l, row)); score wave sw also
+    // stages RoPE tokens 8sw..8sw+7 (lane l: token 8sw + l/8, chunk
+    // swz(l mod 8, token))
+    int loff[NL], rloff = 0;
+#pragma unroll
+    for (int e = 0; e < NL; ++e) loff[e] = swz<CPT>(lane % CPT, kWaves * e + wu) * 16;
+    if constexpr (kScore && DR > 0) rloff = (int)((lane >> 3) * rstr) + swz<8>(lane & 7, 8 * sw + (lane >> 3)) * 16;
+
+    int b = b0, cu = cu0;
+    while (cu < u1) {
+      const int L = p.seqlens[b];
+      const int nb = seq_units(L);
+      const int k0 = 2 * (max(cu, u0) - cu), k1 = 2 * (min(cu + nb, u1) - cu);  // 32-token tiles
+      const int c_first = cu / chunk, c_last = (cu + nb - 1) / chunk;
+      const bool whole = c_first == c_last;
+      if (c == c_first && grp == 0 && tid == 0) {
+        p.meta[2 * b] = b + c_first;
+        p.meta[2 * b + 1] = c_last - c_first + 1;
+      }
+      const int32_t *bt = p.block_table + (long long)b * p.max_pages;
+
+      // ---- rows of this wave: 16-row blocks (score: one, value: two)
+      constexpr int NB = kScore ? 1 : 2;
+      const int r_first = rt * kRows + (kScore ? 16 * sw : 32 * rg);
+      int lim[NB], rowid[NB];
+#pragma unroll
+      for (int nt = 0; nt < NB; ++nt) {
+        const int r = r_first + 16 * nt + n;
+        if (r < p.rows_per_kvh) {
+          const int t = r / p.hpk, h = kvh * p.hpk + r % p.hpk;
+          lim[nt] = p.causal ? L - p.s_q + t + 1 : L;
+          rowid[nt] = (b * p.s_q + t) * p.h_q + h;
+        } else {
+          lim[nt] = L;
+          rowid[nt] = -1;
+        }
+      }
+      const int lim_min = p.causal ? L - p.s_q + r_first / p.hpk + 1 : L;
+
+      // score state: the query of the block, running maximum, row sums;
+      // value state: the output accumulator
+      bf16x8 qreg[kScore ? KS : 1];
+      float m_run = neg_inf(), l_part = 0.f;
+      f32x4 oacc[kScore ? 1 : MTH][2];
+      if constexpr (kScore) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          bf16x8 v = {};
+          if (rowid[0] >= 0) {
+            const bf16 *src = ks < KSN ? qn + (long long)rowid[0] * DK + 32 * ks + 8 * g
+                                       : qr_ + (long long)rowid[0] * DR + 32 * (ks - KSN) + 8 * g;
+            v = *reinterpret_cast<const bf16x8 *>(src);
+          }
+          qreg[ks] = v;
+        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) oacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+
+      // ---- block-table window and tile loads
+      const int npages = L > 0 ? (L + p.page_size - 1) / p.page_size : 0;
+      int win = -(1 << 30), btw = -1;
+      auto page_of = [&](int j) -> int { return p.page_shift >= 0 ? j >> p.page_shift : j / p.page_size; };
+      auto slot_of = [&](int j) -> int {
+        return p.page_shift >= 0 ? j & (p.page_size - 1) : j % p.page_size;
+      };
+      auto ensure_window = [&](int lo, int hi) {
+        if (lo < win || hi >= win + 64) {
+          win = lo;
+          btw = win + lane < npages ? bt[win + lane] : -1;
+        }
+      };
+      const int row_first = L > 0 ? bt[0] * p.page_size : 0;
+      // stage this wave's part of tile k into buf.  A tile on one page uses
+      // one resource per region; otherwise each token row gets its own.
+      // Tokens at or past L read row_first (valid data, masked later).
+      auto load_tile = [&](int k, bf16 *buf) __attribute__((always_inline)) {
+        const int jb = k * kT;
+        if (aligned_pages && jb + kT <= L) {
+          const int pi = jb >> p.page_shift;
+          ensure_window(pi, pi);
+          const int pg = __builtin_amdgcn_readlane(btw, pi - win);
+          const long long row0 = (long long)pg * p.page_size + (jb & (p.page_size - 1));
+          const __amdgpu_buffer_rsrc_t rk = make_rsrc(kcb + row0 * kstr);
+#pragma unroll
+          for (int u = 0; u < NL; ++u) {
+            const int t = kWaves * u + wu;
+            if (CPT == 64 || lane < CPT)
+              lds_dma16(rk, buf + t * DK, static_cast<unsigned>(loff[u]), static_cast<unsigned>(t * kstr));
+          }
+          if constexpr (kScore && DR > 0)
+            lds_dma16(make_rsrc(rcb + row0 * rstr), buf + C::ROFF + 8 * sw * DR, static_cast<unsigned>(rloff),
+                      static_cast<unsigned>(8 * sw * rstr));
+        } else {
+          ensure_window(page_of(jb), page_of(max(jb, min(jb + kT, L) - 1)));
+          const int j = jb + (lane & (kT - 1));
+          const int pg = __shfl(btw, (page_of(j) - win) & 63);
+          const int row_reg = j < L ? pg * p.page_size + slot_of(j) : row_first;
+#pragma unroll
+          for (int u = 0; u < NL; ++u) {
+            const int t = kWaves * u + wu;
+            const long long row = __builtin_amdgcn_readlane(row_reg, t);
+            if (CPT == 64 || lane < CPT)
+              lds_dma16(make_rsrc(kcb + row * kstr), buf + t * DK, static_cast<unsigned>(loff[u]), 0u);
+          }
+          if constexpr (kScore && DR > 0) {
+            // tokens 8sw .. 8sw + 7, one instruction (8 lanes) each
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int t = 8 * sw + i;
+              const long long row = __builtin_amdgcn_readlane(row_reg, t);
+              if (lane < 8)
+                lds_dma16(make_rsrc(rcb + row * rstr), buf + C::ROFF + t * DR,
+                          static_cast<unsigned>(swz<8>(lane, t) * 16), 0u);
+            }
+          }
+        }
+      };
+      auto zero_tile = [&](bf16 *buf) {
+        for (int i = tid; i < C::BUF / 8; i += kThreads) *reinterpret_cast<u32x4 *>(buf + 8 * i) = u32x4{0u, 0u, 0u, 0u};
+      };
+
+      // ---- score stage for tile k in buffer ht: S^T, softmax, hand P over
+      auto score_tile = [&](const bf16 *ht, int k) __attribute__((always_inline)) {
+        const int jb = k * kT;
+        constexpr int PD = 3;
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        bf16x8 kf[PD + 1][2];
+        auto kload = [&](int ks, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const bf16 *src = ks < KSN ? ht + 16 * tt * DK + koff[ks & 7] + 256 * (ks >> 3)
+                                       : ht + C::ROFF + 16 * tt * DR + roff[(ks - KSN) & 1];
+            dst[tt] = *reinterpret_cast<const bf16x8 *>(src);
+          }
+        };
+#pragma unroll
+        for (int ks = 0; ks < PD; ++ks) kload(ks, kf[ks]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + PD < KS) kload(ks + PD, kf[(ks + PD) % (PD + 1)]);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+            sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % (PD + 1)][tt], qreg[ks], sacc[tt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // online softmax (base 2, lazy reference maximum)
+        const int par = k & 1;
+        float x[2][4];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[tt][i] = sacc[tt][i] * p.scale_log2;
+        if (jb + kT > lim_min) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (jb + 16 * tt + 4 * g + i >= lim[0]) x[tt][i] = neg_inf();
+        }
+        float mx = neg_inf();
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[tt][i]);
+        mx = xlane_max16(mx);
+        mx = xlane_max32(mx);
+        // the row's reference maximum moves after it has contributed: its
+        // accumulated output takes the factor alpha (applied by the value
+        // waves)
+        float alpha = 1.f;
+        bool moved = false;
+        if (mx > m_run + kLazy) {
+          alpha = __builtin_amdgcn_exp2f(m_run - mx);
+          moved = m_run != neg_inf();
+          m_run = mx;
+        }
+        const float muse = m_run == neg_inf() ? 0.f : m_run;
+        float sum = 0.f;
+        bf16x8 pb;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float e = __builtin_amdgcn_exp2f(x[tt][i] - muse);
+            sum += e;
+            pb[4 * tt + i] = static_cast<bf16>(e);
+          }
+        l_part = l_part * alpha + sum;
+        *reinterpret_cast<bf16x8 *>(s_px + ((par * 4 + sw) * 64 + lane) * 8) = pb;
+        if (g == 0) s_alpha[par][16 * sw + n] = alpha;
+        const bool any = __builtin_amdgcn_ballot_w64(moved) != 0;
+        if (lane == 0) s_moved[par][sw] = any ? 1 : 0;
+      };
+
+      // ---- value stage for tile k in buffer ht: rescale, O^T += V^T P^T
+      auto value_tile = [&](const bf16 *ht, int k) __attribute__((always_inline)) {
+        const int par = k & 1;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          if (s_moved[par][2 * rg + nt]) {
+            const float a = s_alpha[par][32 * rg + 16 * nt + n];
+#pragma unroll
+            for (int mt = 0; mt < MTH; ++mt) oacc[mt][nt] *= a;
+          }
+        }
+        bf16x8 pb[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          pb[nt] = *reinterpret_cast<const bf16x8 *>(s_px + ((par * 4 + 2 * rg + nt) * 64 + lane) * 8);
+        constexpr int VD = 3;
+        bf16x8 va[VD + 1];
+        auto vload = [&](int ml) __attribute__((always_inline)) {
+          const bf16 *lo = ht + voff[ml % NV] + 256 * (ml / 16);
+          return join(lds_read_tr(lo), lds_read_tr(lo + 16 * DK));
+        };
+#pragma unroll
+        for (int ml = 0; ml < VD; ++ml) va[ml] = vload(ml);
+#pragma unroll
+        for (int ml = 0; ml < MTH; ++ml) {
+          if (ml + VD < MTH) va[(ml + VD) % (VD + 1)] = vload(ml + VD);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            oacc[ml][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ml % (VD + 1)], pb[nt], oacc[ml][nt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+
+      // ---- the pipeline.  Iteration k: score waves on tile k (ring slot
+      // (k - k0) mod 4), value waves on tile k - 1; every wave stages its
+      // part of tile k + 2 (the slot last read by the value waves in
+      // iteration k - 1) and, before the barrier, waits for its part of tile
+      // k + 1.
+      auto buf_of = [&](auto idx_tag) -> bf16 * {
+        constexpr int I = decltype(idx_tag)::value;
+        return I == 0 ? s_b0 : I == 1 ? s_b1 : I == 2 ? s_b2 : s_b3;
+      };
+      // prologue: tiles k0 and k0 + 1 (a sequence with no token zero-fills)
+      if (L > 0) {
+        load_tile(k0, s_b0);
+        load_tile(k0 + 1, s_b1);
+      } else {
+        zero_tile(s_b0);
+        zero_tile(s_b1);
+      }
+      if constexpr (kScore) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qreg[ks]));
+      }
+      wait_vmem<NI>();  // tile k0 landed (tile k0 + 1 may still be in flight)
+      __syncthreads();
+
+      auto iteration = [&](auto r_tag, int k) __attribute__((always_inline)) {
+        constexpr int R = decltype(r_tag)::value;  // (k - k0) mod 4
+        const bool more = k + 2 < k1 && L > 0;
+        if (more) load_tile(k + 2, buf_of(std::integral_constant<int, (R + 2) % kRing>{}));
+        if constexpr (kScore) {
+          if (k < k1) score_tile(buf_of(std::integral_constant<int, R>{}), k);
+        } else {
+          if (k > k0) value_tile(buf_of(std::integral_constant<int, (R + kRing - 1) % kRing>{}), k - 1);
+        }
+        if (more) wait_vmem<NI>();
+        else wait_vmem<0>();
+        __syncthreads();
+      };
+      // k runs k0 .. k1 (the last iteration only finishes the value stage);
+      // unrolled by the ring size so that every buffer is static
+      for (int k = k0; k <= k1; k += kRing) {
+        iteration(std::integral_constant<int, 0>{}, k);
+        if (k + 1 <= k1) iteration(std::integral_constant<int, 1>{}, k + 1);
+        if (k + 2 <= k1) iteration(std::integral_constant<int, 2>{}, k + 2);
+        if (k + 3 <= k1) iteration(std::integral_constant<int, 3>{}, k + 3);
+      }
+
+      // ---- finalize: score waves publish the row sums and write the LSE,
+      // value waves normalize and write their columns
+      if constexpr (kScore) {
+        float v = xlane_sum16(l_part);
+        v = xlane_sum32(v);
+        const float lse_nat = v > 0.f ? (m_run + __log2f(v)) * kLn2 : neg_inf();
+        if (g == 0) s_fin[16 * sw + n] = v;
+        if (rowid[0] >= 0 && g == 0) {
+          if (whole) {
+            if (p.lse) p.lse[rowid[0]] = lse_nat;
+          } else {
+            p.lse_part[rowid[0] + (long long)c * p.s_q * p.h_q] = lse_nat;
+          }
+        }
+      }
+      __syncthreads();
+      if constexpr (!kScore) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          if (rowid[nt] < 0) continue;
+          const float v = s_fin[32 * rg + 16 * nt + n];
+          const float inv = v > 0.f ? 1.f / v : 0.f;
+          const int col0 = 16 * MTH * dh;
+          if (whole) {
+            bf16 *out = static_cast<bf16 *>(p.out) + (long long)rowid[nt] * DK + col0;
+#pragma unroll
+            for (int mt = 0; mt < MTH; ++mt) {
+              bf16x4 o;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) o[i] = static_cast<bf16>(oacc[mt][nt][i] * inv);
+              *reinterpret_cast<bf16x4 *>(out + 16 * mt + 4 * g) = o;
+            }
+          } else {
+            // partial of share c for this sequence: slot b + c
+            float *op = p.o_part + (rowid[nt] + (long long)c * p.s_q * p.h_q) * DK + col0;
+#pragma unroll
+            for (int mt = 0; mt < MTH; ++mt) *reinterpret_cast<f32x4 *>(op + 16 * mt + 4 * g) = oacc[mt][nt] * inv;
+          }
+        }
+      }
+      // LDS (tiles, exchange, row sums) is reused by the next sequence
+      __syncthreads();
+      cu += nb;
+      ++b;
+    }
+  };
+  if (wu < 4) run(std::integral_constant<bool, true>{});
+  else run(std::integral_constant<bool, false>{});
+}
+
+template <int DK, int DR>
+hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
+  const int G = p.n_kvh * p.row_tiles;
+  const int cpad = (p.n_chunks + 7) / 8 * 8;
+  hipLaunchKernelGGL((mla_split_kernel<DK, DR>), dim3(G * cpad), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool mla_split_supported(int dk, int dr) { return (dk == 512 || dk == 256) && (dr == 64 || dr == 0); }
+
+int mla_split_rows() { return kRows; }
+
+hipError_t launch_mla_split(const DecodeParams &p, hipStream_t s) {
+  if (p.dk == 512 && p.dr == 64) return launch_split<512, 64>(p, s);
+  if (p.dk == 512 && p.dr == 0) return launch_split<512, 0>(p, s);
+  if (p.dk == 256 && p.dr == 64) return launch_split<256, 64>(p, s);
+  if (p.dk == 256 && p.dr == 0) return launch_split<256, 0>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lkv
