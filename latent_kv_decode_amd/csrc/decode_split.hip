@@ -38,6 +38,13 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kT = 32;     // tokens per tile
 constexpr int kRing = 4;   // tile buffers
 constexpr int kRows = 64;  // query rows per work-group
+// Who stages the tiles and when: 0 value waves, between their products;
+// 1 all waves, at the start of an iteration; 2 all waves, after their stage;
+// 3 all waves, between their products.
+#ifndef LKV_SPLIT_DMA
+#define LKV_SPLIT_DMA 2
+#endif
+constexpr int kDmaPolicy = LKV_SPLIT_DMA;
 constexpr float kLn2 = 0.693147180559945309f;
 // The softmax reference maximum moves only when a tile's maximum exceeds it
 // by more than this (base-2 units); probabilities stay below 2^kLazy.
@@ -70,6 +77,19 @@ template <int N>
 __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Work-group barrier for the tile loop.  __syncthreads() also fences global
+// memory, and that fence waits for every direct-to-LDS load in flight, which
+// would drain the prefetch at each tile; here each wave retires its own LDS
+// reads and writes (lgkmcnt 0) and has already waited (vmcnt) for the tile
+// loads the next step needs.  The empty asm statements keep the compiler from
+// moving LDS accesses across the barrier.
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Reductions over the four 16-lane groups (partners l ^ 16 and l ^ 32).
@@ -152,9 +172,9 @@ __device__ __forceinline__ const char *uniform_ptr(const char *p) {
 // this MUBUF form the compiler keeps its waits on LDS reads exact while such
 // loads are in flight.  Dword 3: 32-bit data format, no swizzle, no tid add.
 constexpr int kRsrcWord3 = 0x00020000;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(uniform_ptr(base)), (short)0, 0x7fffffff,
-                                           kRsrcWord3);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *base, int range = 0x7fffffff) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(uniform_ptr(base)), (short)0,
+                                           __builtin_amdgcn_readfirstlane(range), kRsrcWord3);
 }
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, bf16 *dst, unsigned voff, unsigned soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
@@ -170,11 +190,11 @@ struct SCfg {
   static constexpr int CPT = DK / 8;          // 16-byte chunks per latent row
   static constexpr int ROFF = kT * DK;        // RoPE region of a tile buffer
   static constexpr int BUF = kT * (DK + DR);  // elements per tile buffer
-  static constexpr int NL = kT / kWaves;      // latent rows staged per wave and tile
-  // RoPE: 8 tokens per score wave and tile, one instruction when the tile is
-  // on one page (eight otherwise; waiting for NIS then waits for more)
-  static constexpr int NIS = NL + (DR > 0 ? 1 : 0);  // tile-load instructions, score wave
-  static constexpr int NIV = NL;                     // tile-load instructions, value wave
+  // Tile loads: loader wave i of n stages latent rows i, i + n, ... and, for
+  // i < 4, RoPE tokens 8i..8i+7 (one instruction when the tile is on one
+  // page, eight otherwise; waiting for NI then waits for more).
+  static constexpr int NLOAD = kDmaPolicy == 0 ? 4 : kWaves;  // loader waves
+  static constexpr int NL = kT / NLOAD;                        // latent rows per loader and tile
   static constexpr int PX = 2 * 4 * 64 * 8;          // P^T exchange [parity][block][lane] 16 B
   static constexpr int LDS_BYTES = (kRing * BUF + PX) * 2 + 2 * 64 * 4 + 2 * 4 * 4 + 64 * 4 + 64;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -183,7 +203,7 @@ struct SCfg {
 template <int DK, int DR>
 __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodeParams p) {
   using C = SCfg<DK, DR>;
-  constexpr int KS = C::KS, KSN = C::KSN, MTH = C::MTH, CPT = C::CPT, NL = C::NL;
+  constexpr int KS = C::KS, KSN = C::KSN, MTH = C::MTH, CPT = C::CPT, NL = C::NL, NLOAD = C::NLOAD;
   // tile ring as distinct LDS objects (loads into one are provably
   // independent of reads of the others)
   __shared__ __attribute__((aligned(16))) bf16 s_b0[C::BUF];
@@ -194,7 +214,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
   __shared__ float s_alpha[2][64];                           // [parity][row]
   __shared__ int s_moved[2][4];                              // [parity][16-row block]
   __shared__ float s_fin[64];                                // row sums
-  int *const s_plan = reinterpret_cast<int *>(s_b3);         // free until the first loads
+  __shared__ int s_plan[kWaves + 2];                         // share plan
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, n = lane & 15;
@@ -223,42 +243,54 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
   // compiled on its own so that only its own state is live.
   auto run = [&](auto role_tag) __attribute__((always_inline)) {
     constexpr bool kScore = decltype(role_tag)::value;
-    constexpr int NI = kScore ? C::NIS : C::NIV;  // this wave's loads per tile
     // score wave sw: rows 16 sw..; value wave vw: rows 32 (vw & 1).. (blocks
     // 2 (vw & 1) + nt), value columns 16 MTH (vw >> 1)..
     const int sw = wu, vw = wu - 4;
     const int rg = vw & 1, dh = vw >> 1;
 
-    // ---- per-lane LDS offsets (elements) of this role's fragment reads
-    //  score: key A operand (token block tt): row 16tt + n, chunk 4ks + g
-    int koff[kScore ? 8 : 1], roff[2];
+    // ---- per-lane LDS offsets (elements) of this role's fragment reads.
+    // The swizzle only flips bits 4..7 of an offset, so the offsets of one
+    // lane differ by an XOR with a constant:
+    //  score: key A operand (token block tt): row 16tt + n, chunk 4ks + g:
+    //         koff0 ^ 32 (ks mod 8), plus 256 (ks / 8);
+    //  value: transpose read of column tile mt = MTH dh + ml: lane (g, n)
+    //         reads row 4g + n/4 (and the same 16 rows on) at columns
+    //         16mt + 4(n%4)..+3: voff0 ^ 16 (ml mod 16), plus 256 (ml / 16).
+    int koff0 = 0, roff[2] = {0, 0}, voff0 = 0;
     if constexpr (kScore) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) koff[e] = n * DK + swz<CPT>(4 * e + g, n) * 8;
+      koff0 = n * DK + swz<CPT>(g, n) * 8;
 #pragma unroll
       for (int e = 0; e < 2; ++e) roff[e] = DR > 0 ? n * DR + swz<8>(4 * e + g, n) * 8 : 0;
-    }
-    //  value: transpose read of global column tile mt = MTH dh + ml: lane
-    //  (g, n) reads row 4g + n/4 (and the same 16 rows on) at columns
-    //  16mt + 4(n%4)..+3; the slot depends on mt mod 16, plus 32 chunks per
-    //  16 tiles
-    constexpr int NV = MTH < 16 ? MTH : 16;
-    int voff[kScore ? 1 : NV];
-    if constexpr (!kScore) {
+    } else {
       const int rv = 4 * g + (n >> 2);
-#pragma unroll
-      for (int j = 0; j < NV; ++j)
-        voff[j] = rv * DK + swz<CPT>(2 * (MTH * dh + j) + ((n & 3) >> 1), rv) * 8 + 4 * (n & 1);
+      voff0 = rv * DK + swz<CPT>(2 * MTH * dh + ((n & 3) >> 1), rv) * 8 + 4 * (n & 1);
     }
-    // tile loads: wave w stages tile rows w and w + 8, ... (one latent row
-    // per instruction; lane l fetches chunk swz(l, row)); score wave sw also
-    // stages RoPE tokens 8sw..8sw+7 (lane l: token 8sw + l/8, chunk
-    // swz(l mod 8, token))
-    int loff[NL], rloff = 0;
-#pragma unroll
-    for (int e = 0; e < NL; ++e) loff[e] = swz<CPT>(lane % CPT, kWaves * e + wu) * 16;
-    if constexpr (kScore && DR > 0) rloff = (int)((lane >> 3) * rstr) + swz<8>(lane & 7, 8 * sw + (lane >> 3)) * 16;
+    // tile loads: one latent row per instruction, lane l fetching chunk
+    // swz(l, row) -- for row NLOAD e + li that is loff0 ^ 32 ((NLOAD e) mod 16)
+    // bytes; RoPE tokens 8li..8li+7 with lane l on token 8li + l/8, chunk
+    // swz(l mod 8, token)
+    constexpr bool kLoader = kDmaPolicy != 0 || !kScore;
+    const int li = kDmaPolicy == 0 ? vw : wu;  // loader index
+    constexpr bool kRope = DR > 0 && (kDmaPolicy == 0 || kScore);
+    constexpr int NI = kLoader ? NL + (kRope ? 1 : 0) : 0;  // this wave's loads per tile
+    int loff0 = 0, rloff = 0;
+    if constexpr (kLoader) {
+      loff0 = swz<CPT>(lane % CPT, li) * 16;
+      if constexpr (kRope) rloff = (int)((lane >> 3) * rstr) + swz<8>(lane & 7, 8 * li + (lane >> 3)) * 16;
+    }
 
+    if constexpr (kLoader) {
+      // One empty-range load (no memory access) into each ring buffer in
+      // ring order, ahead of every path: the compiler's wait placement tracks
+      // direct-to-LDS loads per buffer in order of first use, and a common
+      // order on all paths keeps its waits on LDS reads exact.
+      const __amdgpu_buffer_rsrc_t none = make_rsrc(kcb, 0);
+      lds_dma16(none, s_b0, 0u, 0u);
+      lds_dma16(none, s_b1, 0u, 0u);
+      lds_dma16(none, s_b2, 0u, 0u);
+      lds_dma16(none, s_b3, 0u, 0u);
+      wait_vmem<0>();
+    }
     int b = b0, cu = cu0;
     while (cu < u1) {
       const int L = p.seqlens[b];
@@ -324,72 +356,97 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
         if (lo < win || hi >= win + 64) {
           win = lo;
           btw = win + lane < npages ? bt[win + lane] : -1;
+          // retire this load here: a wait placed at its first use would sit
+          // on every tile's path and drain the tile loads in flight
+          wait_vmem<0>();
         }
       };
       const int row_first = L > 0 ? bt[0] * p.page_size : 0;
-      // stage this wave's part of tile k into buf.  A tile on one page uses
-      // one resource per region; otherwise each token row gets its own.
-      // Tokens at or past L read row_first (valid data, masked later).
-      auto load_tile = [&](int k, bf16 *buf) __attribute__((always_inline)) {
+      // Tile k is staged in pieces: piece e < NL is latent row NLOAD e + li,
+      // piece NL the RoPE tokens.  dma_rows holds the cache row
+      // of token jb + (lane mod 32); tokens at or past L read row_first (valid
+      // data, masked later).  A tile on one page takes its RoPE rows in one
+      // instruction.
+      bool dma_al = false;
+      int dma_rows = 0, dma_range = 0;
+      // a tile past the sequence's share (more == false) is issued with an
+      // empty buffer range: no memory is read and the free slot takes zeros
+      auto dma_prepare = [&](int k, bool more) __attribute__((always_inline)) {
         const int jb = k * kT;
-        if (aligned_pages && jb + kT <= L) {
+        dma_range = more ? 0x7fffffff : 0;
+        dma_al = aligned_pages && jb + kT <= L;
+        if (dma_al) {
           const int pi = jb >> p.page_shift;
           ensure_window(pi, pi);
           const int pg = __builtin_amdgcn_readlane(btw, pi - win);
-          const long long row0 = (long long)pg * p.page_size + (jb & (p.page_size - 1));
-          const __amdgpu_buffer_rsrc_t rk = make_rsrc(kcb + row0 * kstr);
-#pragma unroll
-          for (int u = 0; u < NL; ++u) {
-            const int t = kWaves * u + wu;
-            if (CPT == 64 || lane < CPT)
-              lds_dma16(rk, buf + t * DK, static_cast<unsigned>(loff[u]), static_cast<unsigned>(t * kstr));
-          }
-          if constexpr (kScore && DR > 0)
-            lds_dma16(make_rsrc(rcb + row0 * rstr), buf + C::ROFF + 8 * sw * DR, static_cast<unsigned>(rloff),
-                      static_cast<unsigned>(8 * sw * rstr));
+          dma_rows = pg * p.page_size + (jb & (p.page_size - 1)) + (lane & (kT - 1));
         } else {
           ensure_window(page_of(jb), page_of(max(jb, min(jb + kT, L) - 1)));
           const int j = jb + (lane & (kT - 1));
           const int pg = __shfl(btw, (page_of(j) - win) & 63);
-          const int row_reg = j < L ? pg * p.page_size + slot_of(j) : row_first;
-#pragma unroll
-          for (int u = 0; u < NL; ++u) {
-            const int t = kWaves * u + wu;
-            const long long row = __builtin_amdgcn_readlane(row_reg, t);
-            if (CPT == 64 || lane < CPT)
-              lds_dma16(make_rsrc(kcb + row * kstr), buf + t * DK, static_cast<unsigned>(loff[u]), 0u);
-          }
-          if constexpr (kScore && DR > 0) {
-            // tokens 8sw .. 8sw + 7, one instruction (8 lanes) each
+          dma_rows = j < L ? pg * p.page_size + slot_of(j) : row_first;
+        }
+      };
+      auto dma_piece = [&](int e, bf16 *buf) __attribute__((always_inline)) {
+        if (e < NL) {
+          const int t = NLOAD * e + li;
+          const long long row = __builtin_amdgcn_readlane(dma_rows, t);
+          if (CPT == 64 || lane < CPT)
+            lds_dma16(make_rsrc(kcb + row * kstr, dma_range), buf + t * DK,
+                      static_cast<unsigned>(loff0 ^ (32 * ((NLOAD * e) & 15))), 0u);
+        } else if constexpr (kRope) {
+          if (dma_al) {
+            const long long row = __builtin_amdgcn_readlane(dma_rows, 8 * li);
+            lds_dma16(make_rsrc(rcb + row * rstr, dma_range), buf + C::ROFF + 8 * li * DR,
+                      static_cast<unsigned>(rloff), 0u);
+          } else {
+            // tokens 8li .. 8li + 7, one instruction (8 lanes) each
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-              const int t = 8 * sw + i;
-              const long long row = __builtin_amdgcn_readlane(row_reg, t);
+              const int t = 8 * li + i;
+              const long long row = __builtin_amdgcn_readlane(dma_rows, t);
               if (lane < 8)
-                lds_dma16(make_rsrc(rcb + row * rstr), buf + C::ROFF + t * DR,
+                lds_dma16(make_rsrc(rcb + row * rstr, dma_range), buf + C::ROFF + t * DR,
                           static_cast<unsigned>(swz<8>(lane, t) * 16), 0u);
             }
           }
         }
+      };
+      auto issue_all = [&](bf16 *buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < NI; ++e) dma_piece(e, buf);
+      };
+      auto load_tile = [&](int k, bf16 *buf) __attribute__((always_inline)) {
+        dma_prepare(k, true);
+        issue_all(buf);
       };
       auto zero_tile = [&](bf16 *buf) {
         for (int i = tid; i < C::BUF / 8; i += kThreads) *reinterpret_cast<u32x4 *>(buf + 8 * i) = u32x4{0u, 0u, 0u, 0u};
       };
 
       // ---- score stage for tile k in buffer ht: S^T, softmax, hand P over
-      auto score_tile = [&](const bf16 *ht, int k) __attribute__((always_inline)) {
+      auto score_tile = [&](const bf16 *ht, int k, bf16 *dbuf) __attribute__((always_inline)) {
         const int jb = k * kT;
         constexpr int PD = 3;
         f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
         bf16x8 kf[PD + 1][2];
+        // per-stage copies of the offsets: base + offset sums formed here
+        // (hoisted out of the tile loop they would stay live in registers)
+        int ko0 = koff0, ro[2] = {roff[0], roff[1]};
+        asm volatile("" : "+v"(ko0));
+#pragma unroll
+        for (int e = 0; e < 2; ++e) asm volatile("" : "+v"(ro[e]));
         auto kload = [&](int ks, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
-            const bf16 *src = ks < KSN ? ht + 16 * tt * DK + koff[ks & 7] + 256 * (ks >> 3)
-                                       : ht + C::ROFF + 16 * tt * DR + roff[(ks - KSN) & 1];
+            const bf16 *src = ks < KSN ? ht + 16 * tt * DK + (ko0 ^ (32 * (ks & 7))) + 256 * (ks >> 3)
+                                       : ht + C::ROFF + 16 * tt * DR + ro[(ks - KSN) & 1];
             dst[tt] = *reinterpret_cast<const bf16x8 *>(src);
           }
         };
+        // the score products go first on the SIMD's matrix unit; the value
+        // wave's products fill the softmax that follows
+        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int ks = 0; ks < PD; ++ks) kload(ks, kf[ks]);
 #pragma unroll
@@ -398,8 +455,13 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt)
             sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % (PD + 1)][tt], qreg[ks], sacc[tt], 0, 0, 0);
+          if constexpr (kDmaPolicy == 3) {
+            constexpr int SPER = KS / (NI + 1);
+            if (ks % SPER == SPER - 1 && ks / SPER < NI) dma_piece(ks / SPER, dbuf);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
         // online softmax (base 2, lazy reference maximum)
         const int par = k & 1;
         float x[2][4];
@@ -449,8 +511,11 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
         if (lane == 0) s_moved[par][sw] = any ? 1 : 0;
       };
 
-      // ---- value stage for tile k in buffer ht: rescale, O^T += V^T P^T
-      auto value_tile = [&](const bf16 *ht, int k) __attribute__((always_inline)) {
+      // ---- value stage for tile k in buffer ht: rescale, O^T += V^T P^T.
+      // With dbuf set, the pieces of the tile prepared by dma_prepare are
+      // issued between the products (a burst of loads stalls the issuing
+      // wave until the address unit has taken them).
+      auto value_tile = [&](const bf16 *ht, int k, bf16 *dbuf) __attribute__((always_inline)) {
         const int par = k & 1;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
@@ -464,10 +529,12 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
           pb[nt] = *reinterpret_cast<const bf16x8 *>(s_px + ((par * 4 + 2 * rg + nt) * 64 + lane) * 8);
+        int vo0 = voff0;
+        asm volatile("" : "+v"(vo0));
         constexpr int VD = 3;
         bf16x8 va[VD + 1];
         auto vload = [&](int ml) __attribute__((always_inline)) {
-          const bf16 *lo = ht + voff[ml % NV] + 256 * (ml / 16);
+          const bf16 *lo = ht + (vo0 ^ (16 * (ml & 15))) + 256 * (ml / 16);
           return join(lds_read_tr(lo), lds_read_tr(lo + 16 * DK));
         };
 #pragma unroll
@@ -478,23 +545,31 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
             oacc[ml][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ml % (VD + 1)], pb[nt], oacc[ml][nt], 0, 0, 0);
+          if constexpr (kDmaPolicy == 0 || kDmaPolicy == 3) {
+            constexpr int PER = MTH / NL;  // products between two pieces
+            if (ml % PER == PER - 1) dma_piece(ml / PER, dbuf);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
+        // the RoPE piece last: a wait the compiler places before this tile's
+        // first LDS read then never covers loads issued in this stage
+        if constexpr (kRope && (kDmaPolicy == 0 || kDmaPolicy == 3)) dma_piece(NL, dbuf);
       };
 
       // ---- the pipeline.  Iteration k: score waves on tile k (ring slot
-      // (k - k0) mod 4), value waves on tile k - 1; every wave stages its
-      // part of tile k + 2 (the slot last read by the value waves in
-      // iteration k - 1) and, before the barrier, waits for its part of tile
-      // k + 1.
+      // (k - k0) mod 4), value waves on tile k - 1; the value waves stage
+      // tile k + 2 (into the slot they read in iteration k - 1) and, before
+      // the barrier, wait for their loads of tile k + 1.
       auto buf_of = [&](auto idx_tag) -> bf16 * {
         constexpr int I = decltype(idx_tag)::value;
         return I == 0 ? s_b0 : I == 1 ? s_b1 : I == 2 ? s_b2 : s_b3;
       };
       // prologue: tiles k0 and k0 + 1 (a sequence with no token zero-fills)
       if (L > 0) {
-        load_tile(k0, s_b0);
-        load_tile(k0 + 1, s_b1);
+        if constexpr (kLoader) {
+          load_tile(k0, s_b0);
+          load_tile(k0 + 1, s_b1);
+        }
       } else {
         zero_tile(s_b0);
         zero_tile(s_b1);
@@ -503,30 +578,53 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qreg[ks]));
       }
-      wait_vmem<NI>();  // tile k0 landed (tile k0 + 1 may still be in flight)
-      __syncthreads();
+      wait_vmem<NI>();  // tile k0 landed (k0 + 1 may be in flight)
+      tile_barrier();
 
-      auto iteration = [&](auto r_tag, int k) __attribute__((always_inline)) {
+      auto iteration = [&](auto r_tag, int k, auto first_tag) __attribute__((always_inline)) {
         constexpr int R = decltype(r_tag)::value;  // (k - k0) mod 4
+        constexpr bool kFirst = decltype(first_tag)::value;
         const bool more = k + 2 < k1 && L > 0;
-        if (more) load_tile(k + 2, buf_of(std::integral_constant<int, (R + 2) % kRing>{}));
+        bf16 *const dbuf = buf_of(std::integral_constant<int, (R + 2) % kRing>{});
+        if constexpr (kLoader) dma_prepare(k + 2, more);
+        if constexpr (kLoader && kDmaPolicy == 1) issue_all(dbuf);
         if constexpr (kScore) {
-          if (k < k1) score_tile(buf_of(std::integral_constant<int, R>{}), k);
+          if (k < k1) score_tile(buf_of(std::integral_constant<int, R>{}), k, dbuf);
+          else if constexpr (kDmaPolicy == 3) issue_all(dbuf);
         } else {
-          if (k > k0) value_tile(buf_of(std::integral_constant<int, (R + kRing - 1) % kRing>{}), k - 1);
+          if constexpr (kFirst) {
+            if constexpr (kDmaPolicy == 0 || kDmaPolicy == 3) issue_all(dbuf);
+          } else {
+            value_tile(buf_of(std::integral_constant<int, (R + kRing - 1) % kRing>{}), k - 1, dbuf);
+          }
         }
-        if (more) wait_vmem<NI>();
-        else wait_vmem<0>();
-        __syncthreads();
+        if constexpr (kLoader && kDmaPolicy == 2) issue_all(dbuf);
+        wait_vmem<NI>();
+        tile_barrier();
       };
-      // k runs k0 .. k1 (the last iteration only finishes the value stage);
-      // unrolled by the ring size so that every buffer is static
-      for (int k = k0; k <= k1; k += kRing) {
-        iteration(std::integral_constant<int, 0>{}, k);
-        if (k + 1 <= k1) iteration(std::integral_constant<int, 1>{}, k + 1);
-        if (k + 2 <= k1) iteration(std::integral_constant<int, 2>{}, k + 2);
-        if (k + 3 <= k1) iteration(std::integral_constant<int, 3>{}, k + 3);
+      // k runs k0 .. k1 (the first iteration has no value stage, the last
+      // only the value stage), unrolled by the ring size so that every buffer
+      // is static.  The loop body has no conditional iteration: a path that
+      // skipped one would reach the loop head with another buffer's loads
+      // pending, and the compiler would then wait for those before reading.
+      using std::false_type;
+      using std::integral_constant;
+      iteration(integral_constant<int, 0>{}, k0, std::true_type{});
+      int k = k0 + 1;
+      for (; k + 3 <= k1; k += kRing) {
+        iteration(integral_constant<int, 1>{}, k, false_type{});
+        iteration(integral_constant<int, 2>{}, k + 1, false_type{});
+        iteration(integral_constant<int, 3>{}, k + 2, false_type{});
+        iteration(integral_constant<int, 0>{}, k + 3, false_type{});
       }
+      if (k <= k1) {
+        iteration(integral_constant<int, 1>{}, k, false_type{});
+        if (k + 1 <= k1) {
+          iteration(integral_constant<int, 2>{}, k + 1, false_type{});
+          if (k + 2 <= k1) iteration(integral_constant<int, 3>{}, k + 2, false_type{});
+        }
+      }
+      wait_vmem<0>();  // the empty-range loads of the last tiles
 
       // ---- finalize: score waves publish the row sums and write the LSE,
       // value waves normalize and write their columns
