@@ -70,9 +70,9 @@ struct Shape {
   bool v_alias;
 };
 
-// Kernels for many query rows over one latent head: score and value products
-// on separate waves (split) or on the same waves (wide).
-enum { kLatentNone = 0, kLatentWide = 1, kLatentSplit = 2 };
+// Kernel for many query rows over one latent head (score and value products
+// on separate waves), else the row-tiled kernel.
+enum { kLatentNone = 0, kLatentSplit = 1 };
 
 struct Plan {
   int latent;      // kernel for many rows over one latent (0: the row-tiled kernel)
@@ -89,9 +89,7 @@ lkv_status make_plan(const Shape &s, Plan *pl) {
   pl->latent = kLatentNone;
   if (s.dtype == LKV_BF16 && s.v_alias && rows_per_kvh > 32 && lkv::mla_split_supported(s.dk, s.dr))
     pl->latent = kLatentSplit;
-  pl->rows = pl->latent == kLatentSplit  ? lkv::mla_split_rows()
-             : pl->latent == kLatentWide ? lkv::mla_wide_rows(1)
-                                         : lkv::mfma_decode_rows(rows_per_kvh);
+  pl->rows = pl->latent == kLatentSplit ? lkv::mla_split_rows() : lkv::mfma_decode_rows(rows_per_kvh);
   pl->row_tiles = (rows_per_kvh + pl->rows - 1) / pl->rows;
   int cus = 0;
   if (device_cus(&cus) != 0) return fail(LKV_ERR_HIP, "cannot query the device compute-unit count");
@@ -135,8 +133,8 @@ lkv_status check_shape(const Shape &s) {
   if (s.num_splits < 0) return fail(LKV_ERR_SHAPE, "num_splits %d is negative", s.num_splits);
   if (s.dtype == LKV_BF16) {
     const int rows_per_kvh = s.s_q * (s.h_q / s.n_kvh);
-    const bool wide = s.v_alias && rows_per_kvh > 32 && lkv::mla_split_supported(s.dk, s.dr);
-    if (!wide && !lkv::mfma_decode_supported(s.dk, s.dr, s.dv, s.v_alias, rows_per_kvh))
+    const bool many = s.v_alias && rows_per_kvh > 32 && lkv::mla_split_supported(s.dk, s.dr);
+    if (!many && !lkv::mfma_decode_supported(s.dk, s.dr, s.dv, s.v_alias, rows_per_kvh))
       return fail(LKV_ERR_UNSUPPORTED,
                   "no bf16 kernel for key width %d + RoPE %d, value width %d (%s); compiled: latent "
                   "512+64, 256+64, 128+64, 512+0; grouped 128+64, 128+0, 64+0, 256+0",
@@ -244,9 +242,8 @@ lkv_status run_decode(const Shape &s, const Ptrs &p, float scale) {
   d.meta = reinterpret_cast<int32_t *>(ws + pl.ws_opart + pl.ws_lse);
   if (p.events[0] && (e = hipEventRecord(static_cast<hipEvent_t>(p.events[0]), p.stream)) != hipSuccess)
     return hip_fail(e, "kernel_events[0] record");
-  e = pl.latent == kLatentSplit  ? lkv::launch_mla_split(d, p.stream)
-      : pl.latent == kLatentWide ? lkv::launch_mla_wide(d, 1, p.stream)
-                                 : lkv::launch_mfma_decode(d, s.v_alias, pl.rows, p.stream);
+  e = pl.latent == kLatentSplit ? lkv::launch_mla_split(d, p.stream)
+                                : lkv::launch_mfma_decode(d, s.v_alias, pl.rows, p.stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (p.events[1] && (e = hipEventRecord(static_cast<hipEvent_t>(p.events[1]), p.stream)) != hipSuccess)
     return hip_fail(e, "kernel_events[1] record");

@@ -67,11 +67,6 @@ struct ExpandParams {
 bool mfma_decode_supported(int dk, int dr, int dv, bool v_alias, int rows_per_kvh);
 int mfma_decode_rows(int rows_per_kvh);  // ROWS template used for this problem
 hipError_t launch_mfma_decode(const DecodeParams &p, bool v_alias, int rows, hipStream_t s);
-// Latent path with 64 * nt query rows per work-group (decode_wide.hip),
-// nt in {1, 2}.
-bool mla_wide_supported(int dk, int dr);
-int mla_wide_rows(int nt);
-hipError_t launch_mla_wide(const DecodeParams &p, int nt, hipStream_t s);
 // Latent path with the score and value products on different waves, 64 query
 // rows per work-group (decode_split.hip).
 bool mla_split_supported(int dk, int dr);
