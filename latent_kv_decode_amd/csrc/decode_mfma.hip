@@ -159,6 +159,18 @@ constexpr float kLazy = 8.0f;
 // s_waitcnt vmcnt(0): every direct-to-LDS load of this wave has landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Work-group barrier inside a tile step.  __syncthreads() also fences global
+// memory, and that fence waits for every load in flight -- here the next
+// tile's prefetch, which would then be exposed at every step.  This one
+// retires the wave's LDS accesses (lgkmcnt 0) and meets at s_barrier; the
+// empty asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ s16x4 lds_read_tr(const bf16 *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
 }
@@ -494,7 +506,7 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
         mx = fmaxf(mx, xlane_max32(mx));
         if (g == 0) s_red[w * ROWS + 16 * nt + n] = mx;
       }
-      __syncthreads();
+      lds_barrier();
 
       // ---- online softmax with a lazily moved reference maximum
       bool moved = false;
@@ -531,7 +543,7 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) oacc[mt][nt] *= alpha[nt];
       }
-      __syncthreads();
+      lds_barrier();
 
       // ---- O^T = V^T P^T on this wave's value columns
       const bf16 *vt = VA ? kt : kt + C::VOFF;
