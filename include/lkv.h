@@ -48,7 +48,8 @@
  *    LSE = -inf.  Device-resident values (lengths, table entries) are a
  *    caller contract: 0 <= L_b <= max_pages * page_size and every table entry
  *    of a used page names a page inside the cache.
- *  - Scores are softmax_scale * <q, k>; LSE is the natural log of the sum of
+ *  - Scores are softmax_scale * <q, k>, with softmax_scale positive and
+ *    finite (else LKV_ERR_SHAPE); LSE is the natural log of the sum of
  *    exp(score) over the visible tokens, in float32.
  *  - Outputs have the input dtype; bf16 paths round to nearest even.  bf16
  *    inputs are multiplied on the MFMA units with float32 accumulation; the

@@ -189,6 +189,8 @@ lkv_status check_ptrs(const Shape &s, const Ptrs &p) {
 lkv_status run_decode(const Shape &s, const Ptrs &p, float scale) {
   lkv_status st = check_shape(s);
   if (st != LKV_OK) return st;
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(LKV_ERR_SHAPE, "softmax_scale %g must be positive and finite", (double)scale);
   if (s.B == 0) return LKV_OK;  // nothing to compute; pointers of empty tensors may be NULL
   if ((st = check_ptrs(s, p)) != LKV_OK) return st;
   Plan pl;

@@ -4,21 +4,23 @@
 // the shared RoPE key, and the latent is also the value].
 //
 // A work-group takes 64 query rows of one latent head and a share of the
-// batch's cache tiles.  Its eight waves split the work by stage:
-//   waves 0..3  (score waves) hold the query of 16 rows each in registers and
+// batch's cache tiles.  Its eight waves split the work by stage; wave w runs
+// on SIMD w mod 4, so every SIMD hosts one wave of each role:
+//   waves 0..3  (score) hold the query of 16 rows each in registers and
 //               compute S^T = K Q^T per 32-token tile, the online softmax
 //               (running maximum, row sums) and P = exp(S - m) in bf16;
-//   waves 4..7  (value waves) hold the output accumulator (fp32, transposed)
-//               of 32 rows x half of the value columns each and compute
-//               O^T += V^T P^T.
+//   waves 4..7  (value) hold the output accumulator (fp32, transposed) of all
+//               64 rows for a quarter of the value columns and compute
+//               O^T += V^T P^T -- every value fragment read from LDS feeds
+//               four row blocks.
 // P (already in the MFMA operand layout) and the per-row rescale factors go
 // from score to value waves through LDS, one tile behind: in iteration k the
 // score waves work on tile k while the value waves work on tile k - 1, and
-// one barrier per tile hands P over.  Each SIMD runs one score and one value
-// wave, so the softmax of one overlaps the MFMAs of the other, and each value
-// fragment read from LDS feeds two MFMAs (two 16-row blocks).  Tiles (32
-// tokens) are staged by direct-to-LDS buffer loads into a ring of four
-// buffers, two tiles ahead of the score waves.
+// one barrier per tile hands P over.  The softmax of one role overlaps the
+// matrix products of the other on each SIMD.  Tiles (32 tokens) are staged
+// by direct-to-LDS buffer loads into a ring of four buffers, two tiles ahead;
+// the value waves issue their share of a tile before their products, the
+// score waves after theirs.
 #include <type_traits>
 
 #include "lkv_internal.h"
@@ -38,17 +40,11 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kT = 32;     // tokens per tile
 constexpr int kRing = 4;   // tile buffers
 constexpr int kRows = 64;  // query rows per work-group
-// Who stages the tiles and when: 0 value waves, between their products;
-// 1 all waves, at the start of an iteration; 2 all waves, after their stage;
-// 3 all waves, between their products.
-#ifndef LKV_SPLIT_DMA
-#define LKV_SPLIT_DMA 2
-#endif
-constexpr int kDmaPolicy = LKV_SPLIT_DMA;
 constexpr float kLn2 = 0.693147180559945309f;
 // The softmax reference maximum moves only when a tile's maximum exceeds it
 // by more than this (base-2 units); probabilities stay below 2^kLazy.
 constexpr float kLazy = 8.0f;
+
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -82,9 +78,9 @@ __device__ __forceinline__ void wait_vmem() {
 // Work-group barrier for the tile loop.  __syncthreads() also fences global
 // memory, and that fence waits for every direct-to-LDS load in flight, which
 // would drain the prefetch at each tile; here each wave retires its own LDS
-// reads and writes (lgkmcnt 0) and has already waited (vmcnt) for the tile
-// loads the next step needs.  The empty asm statements keep the compiler from
-// moving LDS accesses across the barrier.
+// reads and writes (lgkmcnt 0) and the load waves have already waited (vmcnt)
+// for the tile the next step needs.  The empty asm statements keep the
+// compiler from moving LDS accesses across the barrier.
 __device__ __forceinline__ void tile_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   asm volatile("" ::: "memory");
@@ -171,6 +167,8 @@ __device__ __forceinline__ const char *uniform_ptr(const char *p) {
 // Direct-to-LDS loads through raw buffer resources (buffer_load ... lds): with
 // this MUBUF form the compiler keeps its waits on LDS reads exact while such
 // loads are in flight.  Dword 3: 32-bit data format, no swizzle, no tid add.
+// A range of 0 makes every lane out of range: nothing is read from memory
+// and the LDS destination receives zeros.
 constexpr int kRsrcWord3 = 0x00020000;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *base, int range = 0x7fffffff) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(uniform_ptr(base)), (short)0,
@@ -185,17 +183,16 @@ struct SCfg {
   static_assert((DK == 512 || DK == 256) && (DR == 0 || DR == 64), "widths");
   static constexpr int KS = (DK + DR) / 32;   // QK^T k-steps
   static constexpr int KSN = DK / 32;         // of which on the latent
-  static constexpr int MT = DK / 16;          // value column tiles
-  static constexpr int MTH = MT / 2;          // per value wave (half of the columns)
+  static constexpr int MTV = DK / 64;         // value column tiles per value wave
   static constexpr int CPT = DK / 8;          // 16-byte chunks per latent row
   static constexpr int ROFF = kT * DK;        // RoPE region of a tile buffer
   static constexpr int BUF = kT * (DK + DR);  // elements per tile buffer
-  // Tile loads: loader wave i of n stages latent rows i, i + n, ... and, for
-  // i < 4, RoPE tokens 8i..8i+7 (one instruction when the tile is on one
-  // page, eight otherwise; waiting for NI then waits for more).
-  static constexpr int NLOAD = kDmaPolicy == 0 ? 4 : kWaves;  // loader waves
-  static constexpr int NL = kT / NLOAD;                        // latent rows per loader and tile
-  static constexpr int PX = 2 * 4 * 64 * 8;          // P^T exchange [parity][block][lane] 16 B
+  // tile loads: every wave stages 4 latent rows (one instruction each); with
+  // a RoPE key each score wave also stages 8 RoPE rows (one instruction when
+  // the tile is on one page, eight otherwise; waiting for the count then
+  // waits for more)
+  static constexpr int NLL = kT / kWaves;
+  static constexpr int PX = 2 * 4 * 64 * 8;  // P^T exchange [parity][row block][lane] 16 B
   static constexpr int LDS_BYTES = (kRing * BUF + PX) * 2 + 2 * 64 * 4 + 2 * 4 * 4 + 64 * 4 + 64;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
@@ -203,7 +200,7 @@ struct SCfg {
 template <int DK, int DR>
 __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodeParams p) {
   using C = SCfg<DK, DR>;
-  constexpr int KS = C::KS, KSN = C::KSN, MTH = C::MTH, CPT = C::CPT, NL = C::NL, NLOAD = C::NLOAD;
+  constexpr int KS = C::KS, KSN = C::KSN, MTV = C::MTV, CPT = C::CPT, NLL = C::NLL;
   // tile ring as distinct LDS objects (loads into one are provably
   // independent of reads of the others)
   __shared__ __attribute__((aligned(16))) bf16 s_b0[C::BUF];
@@ -242,44 +239,39 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
   // The two roles run the same loop (same tiles, same barriers); each is
   // compiled on its own so that only its own state is live.
   auto run = [&](auto role_tag) __attribute__((always_inline)) {
-    constexpr bool kScore = decltype(role_tag)::value;
-    // score wave sw: rows 16 sw..; value wave vw: rows 32 (vw & 1).. (blocks
-    // 2 (vw & 1) + nt), value columns 16 MTH (vw >> 1)..
+    constexpr bool kScore = decltype(role_tag)::value, kValue = !kScore;
+    constexpr int NI = NLL + (kScore && DR > 0 ? 1 : 0);  // this wave's loads per tile
+    // score wave sw: rows 16 sw .. (row block sw); value wave vw: value
+    // columns 16 MTV vw ..
     const int sw = wu, vw = wu - 4;
-    const int rg = vw & 1, dh = vw >> 1;
 
     // ---- per-lane LDS offsets (elements) of this role's fragment reads.
     // The swizzle only flips bits 4..7 of an offset, so the offsets of one
     // lane differ by an XOR with a constant:
     //  score: key A operand (token block tt): row 16tt + n, chunk 4ks + g:
     //         koff0 ^ 32 (ks mod 8), plus 256 (ks / 8);
-    //  value: transpose read of column tile mt = MTH dh + ml: lane (g, n)
-    //         reads row 4g + n/4 (and the same 16 rows on) at columns
-    //         16mt + 4(n%4)..+3: voff0 ^ 16 (ml mod 16), plus 256 (ml / 16).
+    //  value: transpose read of column tile MTV vw + mt: lane (g, n) reads
+    //         row 4g + n/4 (and the same 16 rows on) at columns 16 (MTV vw +
+    //         mt) + 4(n%4)..+3: voff0 ^ 16 mt.
     int koff0 = 0, roff[2] = {0, 0}, voff0 = 0;
     if constexpr (kScore) {
       koff0 = n * DK + swz<CPT>(g, n) * 8;
 #pragma unroll
       for (int e = 0; e < 2; ++e) roff[e] = DR > 0 ? n * DR + swz<8>(4 * e + g, n) * 8 : 0;
-    } else {
+    } else if constexpr (kValue) {
       const int rv = 4 * g + (n >> 2);
-      voff0 = rv * DK + swz<CPT>(2 * MTH * dh + ((n & 3) >> 1), rv) * 8 + 4 * (n & 1);
-    }
-    // tile loads: one latent row per instruction, lane l fetching chunk
-    // swz(l, row) -- for row NLOAD e + li that is loff0 ^ 32 ((NLOAD e) mod 16)
-    // bytes; RoPE tokens 8li..8li+7 with lane l on token 8li + l/8, chunk
-    // swz(l mod 8, token)
-    constexpr bool kLoader = kDmaPolicy != 0 || !kScore;
-    const int li = kDmaPolicy == 0 ? vw : wu;  // loader index
-    constexpr bool kRope = DR > 0 && (kDmaPolicy == 0 || kScore);
-    constexpr int NI = kLoader ? NL + (kRope ? 1 : 0) : 0;  // this wave's loads per tile
-    int loff0 = 0, rloff = 0;
-    if constexpr (kLoader) {
-      loff0 = swz<CPT>(lane % CPT, li) * 16;
-      if constexpr (kRope) rloff = (int)((lane >> 3) * rstr) + swz<8>(lane & 7, 8 * li + (lane >> 3)) * 16;
+      voff0 = rv * DK + swz<CPT>(2 * MTV * vw + ((n & 3) >> 1), rv) * 8 + 4 * (n & 1);
     }
 
-    if constexpr (kLoader) {
+    // tile loads: lane offsets of latent row 8e + wu (they depend on e mod
+    // 2) and, for a score wave, of RoPE rows 8 sw .. 8 sw + 7, relative to a
+    // tile's first row
+    int lofs[2], rofs = 0;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) lofs[e] = swz<CPT>(lane % CPT, kWaves * e + wu) * 16;
+    if constexpr (kScore && DR > 0) rofs = (int)((lane >> 3) * rstr) + swz<8>(lane & 7, 8 * sw + (lane >> 3)) * 16;
+
+    {
       // One empty-range load (no memory access) into each ring buffer in
       // ring order, ahead of every path: the compiler's wait placement tracks
       // direct-to-LDS loads per buffer in order of first use, and a common
@@ -291,6 +283,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
       lds_dma16(none, s_b3, 0u, 0u);
       wait_vmem<0>();
     }
+
     int b = b0, cu = cu0;
     while (cu < u1) {
       const int L = p.seqlens[b];
@@ -302,15 +295,14 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
         p.meta[2 * b] = b + c_first;
         p.meta[2 * b + 1] = c_last - c_first + 1;
       }
-      const int32_t *bt = p.block_table + (long long)b * p.max_pages;
 
-      // ---- rows of this wave: 16-row blocks (score: one, value: two)
-      constexpr int NB = kScore ? 1 : 2;
-      const int r_first = rt * kRows + (kScore ? 16 * sw : 32 * rg);
+      // ---- rows: a score wave owns one row block, a value wave all 4
+      constexpr int NB = kScore ? 1 : 4;
+      const int rb0 = kScore ? sw : 0;  // first row block
       int lim[NB], rowid[NB];
 #pragma unroll
       for (int nt = 0; nt < NB; ++nt) {
-        const int r = r_first + 16 * nt + n;
+        const int r = rt * kRows + 16 * (rb0 + nt) + n;
         if (r < p.rows_per_kvh) {
           const int t = r / p.hpk, h = kvh * p.hpk + r % p.hpk;
           lim[nt] = p.causal ? L - p.s_q + t + 1 : L;
@@ -320,13 +312,13 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
           rowid[nt] = -1;
         }
       }
-      const int lim_min = p.causal ? L - p.s_q + r_first / p.hpk + 1 : L;
+      const int lim_min = p.causal ? L - p.s_q + (rt * kRows + 16 * rb0) / p.hpk + 1 : L;
 
-      // score state: the query of the block, running maximum, row sums;
+      // score state: the query of the rows, running maxima, row sums;
       // value state: the output accumulator
       bf16x8 qreg[kScore ? KS : 1];
       float m_run = neg_inf(), l_part = 0.f;
-      f32x4 oacc[kScore ? 1 : MTH][2];
+      f32x4 oacc[kValue ? MTV : 1][kValue ? 4 : 1];
       if constexpr (kScore) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -340,12 +332,13 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
         }
       } else {
 #pragma unroll
-        for (int mt = 0; mt < MTH; ++mt)
+        for (int mt = 0; mt < MTV; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) oacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int rb = 0; rb < 4; ++rb) oacc[mt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
 
       // ---- block-table window and tile loads
+      const int32_t *bt = p.block_table + (long long)b * p.max_pages;
       const int npages = L > 0 ? (L + p.page_size - 1) / p.page_size : 0;
       int win = -(1 << 30), btw = -1;
       auto page_of = [&](int j) -> int { return p.page_shift >= 0 ? j >> p.page_shift : j / p.page_size; };
@@ -362,15 +355,13 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
         }
       };
       const int row_first = L > 0 ? bt[0] * p.page_size : 0;
-      // Tile k is staged in pieces: piece e < NL is latent row NLOAD e + li,
-      // piece NL the RoPE tokens.  dma_rows holds the cache row
-      // of token jb + (lane mod 32); tokens at or past L read row_first (valid
-      // data, masked later).  A tile on one page takes its RoPE rows in one
-      // instruction.
+      // Tile k: this wave stages latent rows 8e + wu and, for a score wave,
+      // RoPE rows 8 sw .. +7.  dma_rows holds the cache row of token jb +
+      // (lane mod 32); tokens at or past L read row_first (valid data, masked
+      // later).  A tile past the share (more == false) is issued with an empty
+      // buffer range: no memory is read and the free slot takes zeros.
       bool dma_al = false;
       int dma_rows = 0, dma_range = 0;
-      // a tile past the sequence's share (more == false) is issued with an
-      // empty buffer range: no memory is read and the free slot takes zeros
       auto dma_prepare = [&](int k, bool more) __attribute__((always_inline)) {
         const int jb = k * kT;
         dma_range = more ? 0x7fffffff : 0;
@@ -387,45 +378,50 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
           dma_rows = j < L ? pg * p.page_size + slot_of(j) : row_first;
         }
       };
-      auto dma_piece = [&](int e, bf16 *buf) __attribute__((always_inline)) {
-        if (e < NL) {
-          const int t = NLOAD * e + li;
+      auto issue_tile = [&](bf16 *buf) __attribute__((always_inline)) {
+        if (dma_al) {
+          // whole tile on one page, rows row0 .. row0 + 31: one resource per
+          // region and the row offset as the scalar offset, so a load costs
+          // no vector instruction
+          const long long row0 = __builtin_amdgcn_readlane(dma_rows, 0);
+          const __amdgpu_buffer_rsrc_t rk = make_rsrc(kcb + row0 * kstr, dma_range);
+#pragma unroll
+          for (int e = 0; e < NLL; ++e) {
+            const int t = kWaves * e + wu;
+            if (CPT == 64 || lane < CPT)
+              lds_dma16(rk, buf + t * DK, static_cast<unsigned>(lofs[e & 1]), static_cast<unsigned>(t * kstr));
+          }
+          if constexpr (kScore && DR > 0)
+            lds_dma16(make_rsrc(rcb + row0 * rstr, dma_range), buf + C::ROFF + 8 * sw * DR,
+                      static_cast<unsigned>(rofs), static_cast<unsigned>(8 * sw * rstr));
+          return;
+        }
+#pragma unroll
+        for (int e = 0; e < NLL; ++e) {
+          const int t = kWaves * e + wu;
           const long long row = __builtin_amdgcn_readlane(dma_rows, t);
           if (CPT == 64 || lane < CPT)
-            lds_dma16(make_rsrc(kcb + row * kstr, dma_range), buf + t * DK,
-                      static_cast<unsigned>(loff0 ^ (32 * ((NLOAD * e) & 15))), 0u);
-        } else if constexpr (kRope) {
-          if (dma_al) {
-            const long long row = __builtin_amdgcn_readlane(dma_rows, 8 * li);
-            lds_dma16(make_rsrc(rcb + row * rstr, dma_range), buf + C::ROFF + 8 * li * DR,
-                      static_cast<unsigned>(rloff), 0u);
-          } else {
-            // tokens 8li .. 8li + 7, one instruction (8 lanes) each
+            lds_dma16(make_rsrc(kcb + row * kstr, dma_range), buf + t * DK, static_cast<unsigned>(lofs[e & 1]), 0u);
+        }
+        if constexpr (kScore && DR > 0) {
+          // one instruction (8 lanes) per row
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const int t = 8 * li + i;
-              const long long row = __builtin_amdgcn_readlane(dma_rows, t);
-              if (lane < 8)
-                lds_dma16(make_rsrc(rcb + row * rstr, dma_range), buf + C::ROFF + t * DR,
-                          static_cast<unsigned>(swz<8>(lane, t) * 16), 0u);
-            }
+          for (int q = 0; q < 8; ++q) {
+            const int t = 8 * sw + q;
+            const long long row = __builtin_amdgcn_readlane(dma_rows, t);
+            if (lane < 8)
+              lds_dma16(make_rsrc(rcb + row * rstr, dma_range), buf + C::ROFF + t * DR,
+                        static_cast<unsigned>(swz<8>(lane, t) * 16), 0u);
           }
         }
-      };
-      auto issue_all = [&](bf16 *buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int e = 0; e < NI; ++e) dma_piece(e, buf);
-      };
-      auto load_tile = [&](int k, bf16 *buf) __attribute__((always_inline)) {
-        dma_prepare(k, true);
-        issue_all(buf);
       };
       auto zero_tile = [&](bf16 *buf) {
         for (int i = tid; i < C::BUF / 8; i += kThreads) *reinterpret_cast<u32x4 *>(buf + 8 * i) = u32x4{0u, 0u, 0u, 0u};
       };
 
-      // ---- score stage for tile k in buffer ht: S^T, softmax, hand P over
-      auto score_tile = [&](const bf16 *ht, int k, bf16 *dbuf) __attribute__((always_inline)) {
+      // ---- score stage for tile k in buffer ht: S^T for the wave's 16 rows,
+      // softmax, hand P over
+      auto score_tile = [&](const bf16 *ht, int k) __attribute__((always_inline)) {
         const int jb = k * kT;
         constexpr int PD = 3;
         f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -444,9 +440,6 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
             dst[tt] = *reinterpret_cast<const bf16x8 *>(src);
           }
         };
-        // the score products go first on the SIMD's matrix unit; the value
-        // wave's products fill the softmax that follows
-        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int ks = 0; ks < PD; ++ks) kload(ks, kf[ks]);
 #pragma unroll
@@ -455,34 +448,30 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt)
             sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % (PD + 1)][tt], qreg[ks], sacc[tt], 0, 0, 0);
-          if constexpr (kDmaPolicy == 3) {
-            constexpr int SPER = KS / (NI + 1);
-            if (ks % SPER == SPER - 1 && ks / SPER < NI) dma_piece(ks / SPER, dbuf);
-          }
           __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_s_setprio(0);
-        // online softmax (base 2, lazy reference maximum)
+        // online softmax (base 2, lazy reference maximum).  The scale
+        // (positive) is applied to the row maximum and inside the exponent's
+        // fused multiply-add, not to every score.
         const int par = k & 1;
-        float x[2][4];
+        const float sc = p.scale_log2;
+        float y[2][4];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[tt][i] = sacc[tt][i] * p.scale_log2;
-        if (jb + kT > lim_min) {
+          for (int i = 0; i < 4; ++i) y[tt][i] = sacc[tt][i];
+        if (__builtin_expect(jb + kT > lim_min, 0)) {  // the tile crosses a row's visible length
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (jb + 16 * tt + 4 * g + i >= lim[0]) x[tt][i] = neg_inf();
+              if (jb + 16 * tt + 4 * g + i >= lim[0]) y[tt][i] = neg_inf();
         }
-        float mx = neg_inf();
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[tt][i]);
-        mx = xlane_max16(mx);
-        mx = xlane_max32(mx);
+        float ym = fmaxf(fmaxf(fmaxf(y[0][0], y[0][1]), fmaxf(y[0][2], y[0][3])),
+                         fmaxf(fmaxf(y[1][0], y[1][1]), fmaxf(y[1][2], y[1][3])));
+        ym = xlane_max16(ym);
+        ym = xlane_max32(ym);
+        const float mx = ym * sc;
         // the row's reference maximum moves after it has contributed: its
         // accumulated output takes the factor alpha (applied by the value
         // waves)
@@ -500,7 +489,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float e = __builtin_amdgcn_exp2f(x[tt][i] - muse);
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(y[tt][i], sc, -muse));
             sum += e;
             pb[4 * tt + i] = static_cast<bf16>(e);
           }
@@ -511,65 +500,55 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
         if (lane == 0) s_moved[par][sw] = any ? 1 : 0;
       };
 
-      // ---- value stage for tile k in buffer ht: rescale, O^T += V^T P^T.
-      // With dbuf set, the pieces of the tile prepared by dma_prepare are
-      // issued between the products (a burst of loads stalls the issuing
-      // wave until the address unit has taken them).
-      auto value_tile = [&](const bf16 *ht, int k, bf16 *dbuf) __attribute__((always_inline)) {
+      // ---- value stage for tile k in buffer ht: rescale, O^T += V^T P^T
+      auto value_tile = [&](const bf16 *ht, int k) __attribute__((always_inline)) {
         const int par = k & 1;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          if (s_moved[par][2 * rg + nt]) {
-            const float a = s_alpha[par][32 * rg + 16 * nt + n];
+        for (int rb = 0; rb < 4; ++rb) {
+          if (s_moved[par][rb]) {
+            const float a = s_alpha[par][16 * rb + n];
 #pragma unroll
-            for (int mt = 0; mt < MTH; ++mt) oacc[mt][nt] *= a;
+            for (int mt = 0; mt < MTV; ++mt) oacc[mt][rb] *= a;
           }
         }
-        bf16x8 pb[2];
+        bf16x8 pb[4];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          pb[nt] = *reinterpret_cast<const bf16x8 *>(s_px + ((par * 4 + 2 * rg + nt) * 64 + lane) * 8);
+        for (int rb = 0; rb < 4; ++rb)
+          pb[rb] = *reinterpret_cast<const bf16x8 *>(s_px + ((par * 4 + rb) * 64 + lane) * 8);
         int vo0 = voff0;
         asm volatile("" : "+v"(vo0));
         constexpr int VD = 3;
         bf16x8 va[VD + 1];
-        auto vload = [&](int ml) __attribute__((always_inline)) {
-          const bf16 *lo = ht + (vo0 ^ (16 * (ml & 15))) + 256 * (ml / 16);
+        auto vload = [&](int mt) __attribute__((always_inline)) {
+          const bf16 *lo = ht + (vo0 ^ (16 * mt));
           return join(lds_read_tr(lo), lds_read_tr(lo + 16 * DK));
         };
 #pragma unroll
-        for (int ml = 0; ml < VD; ++ml) va[ml] = vload(ml);
+        for (int mt = 0; mt < VD && mt < MTV; ++mt) va[mt] = vload(mt);
 #pragma unroll
-        for (int ml = 0; ml < MTH; ++ml) {
-          if (ml + VD < MTH) va[(ml + VD) % (VD + 1)] = vload(ml + VD);
+        for (int mt = 0; mt < MTV; ++mt) {
+          if (mt + VD < MTV) va[(mt + VD) % (VD + 1)] = vload(mt + VD);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            oacc[ml][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ml % (VD + 1)], pb[nt], oacc[ml][nt], 0, 0, 0);
-          if constexpr (kDmaPolicy == 0 || kDmaPolicy == 3) {
-            constexpr int PER = MTH / NL;  // products between two pieces
-            if (ml % PER == PER - 1) dma_piece(ml / PER, dbuf);
-          }
+          for (int rb = 0; rb < 4; ++rb)
+            oacc[mt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mt % (VD + 1)], pb[rb], oacc[mt][rb], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
-        // the RoPE piece last: a wait the compiler places before this tile's
-        // first LDS read then never covers loads issued in this stage
-        if constexpr (kRope && (kDmaPolicy == 0 || kDmaPolicy == 3)) dma_piece(NL, dbuf);
       };
 
       // ---- the pipeline.  Iteration k: score waves on tile k (ring slot
-      // (k - k0) mod 4), value waves on tile k - 1; the value waves stage
-      // tile k + 2 (into the slot they read in iteration k - 1) and, before
-      // the barrier, wait for their loads of tile k + 1.
+      // (k - k0) mod 4), value waves on tile k - 1; every wave stages its part
+      // of tile k + 2 (into the slot the value waves read in iteration k - 1)
+      // and, before the barrier, waits for its part of tile k + 1.
       auto buf_of = [&](auto idx_tag) -> bf16 * {
         constexpr int I = decltype(idx_tag)::value;
         return I == 0 ? s_b0 : I == 1 ? s_b1 : I == 2 ? s_b2 : s_b3;
       };
       // prologue: tiles k0 and k0 + 1 (a sequence with no token zero-fills)
       if (L > 0) {
-        if constexpr (kLoader) {
-          load_tile(k0, s_b0);
-          load_tile(k0 + 1, s_b1);
-        }
+        dma_prepare(k0, true);
+        issue_tile(s_b0);
+        dma_prepare(k0 + 1, true);
+        issue_tile(s_b1);
       } else {
         zero_tile(s_b0);
         zero_tile(s_b1);
@@ -584,21 +563,19 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
       auto iteration = [&](auto r_tag, int k, auto first_tag) __attribute__((always_inline)) {
         constexpr int R = decltype(r_tag)::value;  // (k - k0) mod 4
         constexpr bool kFirst = decltype(first_tag)::value;
-        const bool more = k + 2 < k1 && L > 0;
-        bf16 *const dbuf = buf_of(std::integral_constant<int, (R + 2) % kRing>{});
-        if constexpr (kLoader) dma_prepare(k + 2, more);
-        if constexpr (kLoader && kDmaPolicy == 1) issue_all(dbuf);
+        // The value waves stage their part first and the score waves theirs
+        // last: the loads of one role are issued while the other role's
+        // products run on the same SIMD (a load stalls its wave while the
+        // address unit is busy).
         if constexpr (kScore) {
-          if (k < k1) score_tile(buf_of(std::integral_constant<int, R>{}), k, dbuf);
-          else if constexpr (kDmaPolicy == 3) issue_all(dbuf);
+          if (k < k1) score_tile(buf_of(std::integral_constant<int, R>{}), k);
+          dma_prepare(k + 2, k + 2 < k1 && L > 0);
+          issue_tile(buf_of(std::integral_constant<int, (R + 2) % kRing>{}));
         } else {
-          if constexpr (kFirst) {
-            if constexpr (kDmaPolicy == 0 || kDmaPolicy == 3) issue_all(dbuf);
-          } else {
-            value_tile(buf_of(std::integral_constant<int, (R + kRing - 1) % kRing>{}), k - 1, dbuf);
-          }
+          dma_prepare(k + 2, k + 2 < k1 && L > 0);
+          issue_tile(buf_of(std::integral_constant<int, (R + 2) % kRing>{}));
+          if constexpr (!kFirst) value_tile(buf_of(std::integral_constant<int, (R + kRing - 1) % kRing>{}), k - 1);
         }
-        if constexpr (kLoader && kDmaPolicy == 2) issue_all(dbuf);
         wait_vmem<NI>();
         tile_barrier();
       };
@@ -642,27 +619,27 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
         }
       }
       __syncthreads();
-      if constexpr (!kScore) {
+      if constexpr (kValue) {
+        const int col0 = 16 * MTV * vw;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          if (rowid[nt] < 0) continue;
-          const float v = s_fin[32 * rg + 16 * nt + n];
+        for (int rb = 0; rb < 4; ++rb) {
+          if (rowid[rb] < 0) continue;
+          const float v = s_fin[16 * rb + n];
           const float inv = v > 0.f ? 1.f / v : 0.f;
-          const int col0 = 16 * MTH * dh;
           if (whole) {
-            bf16 *out = static_cast<bf16 *>(p.out) + (long long)rowid[nt] * DK + col0;
+            bf16 *out = static_cast<bf16 *>(p.out) + (long long)rowid[rb] * DK + col0;
 #pragma unroll
-            for (int mt = 0; mt < MTH; ++mt) {
+            for (int mt = 0; mt < MTV; ++mt) {
               bf16x4 o;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) o[i] = static_cast<bf16>(oacc[mt][nt][i] * inv);
+              for (int i = 0; i < 4; ++i) o[i] = static_cast<bf16>(oacc[mt][rb][i] * inv);
               *reinterpret_cast<bf16x4 *>(out + 16 * mt + 4 * g) = o;
             }
           } else {
             // partial of share c for this sequence: slot b + c
-            float *op = p.o_part + (rowid[nt] + (long long)c * p.s_q * p.h_q) * DK + col0;
+            float *op = p.o_part + (rowid[rb] + (long long)c * p.s_q * p.h_q) * DK + col0;
 #pragma unroll
-            for (int mt = 0; mt < MTH; ++mt) *reinterpret_cast<f32x4 *>(op + 16 * mt + 4 * g) = oacc[mt][nt] * inv;
+            for (int mt = 0; mt < MTV; ++mt) *reinterpret_cast<f32x4 *>(op + 16 * mt + 4 * g) = oacc[mt][rb] * inv;
           }
         }
       }

@@ -105,6 +105,10 @@ def _status(lib, a):
     (dict(kv_tok_stride=256), 2),
     (dict(workspace=None), 5),
     (dict(workspace=FAKE + 16), 4),
+    (dict(softmax_scale=0.0), 2),
+    (dict(softmax_scale=-0.05), 2),
+    (dict(softmax_scale=float("inf")), 2),
+    (dict(softmax_scale=float("nan")), 2),
 ])
 def test_mla_validation(lib, change, expect):
     st = _status(lib, _mla(**change))
@@ -141,7 +145,8 @@ def _gqa(**kw):
 
 @pytest.mark.parametrize("change,expect", [
     (dict(h_q=30), 2), (dict(d_h=96), 3), (dict(v_cache=None), 1), (dict(q_rope=FAKE), 2),
-    (dict(d_rope=64), 1), (dict(v_tok_stride=512), 2), (dict(k_tok_stride=1028), 4)])
+    (dict(d_rope=64), 1), (dict(v_tok_stride=512), 2), (dict(k_tok_stride=1028), 4),
+    (dict(softmax_scale=-1.0), 2)])
 def test_gqa_validation(lib, change, expect):
     st = lib.lkv_gqa_decode(ctypes.byref(_gqa(**change)))
     assert st == expect, (st, lkv.lkv_last_error())
