@@ -8,7 +8,8 @@
 // computation only as one softmax over the whole cache, and the merge follows
 // from writing that softmax over a partition of the cache.
 //
-// One wave per (b, t, h) row; lanes stride over the value columns in float4.
+// One wave per (b, t, h) row; lanes stride over the value columns in float4,
+// and the weights of up to 64 works sit one per lane.
 #include "lkv_internal.h"
 
 namespace lkv {
@@ -16,7 +17,6 @@ namespace {
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-constexpr int kMaxWorks = 64;  // per-lane cache of weights; more works loop
 
 __global__ void __launch_bounds__(256) combine_kernel(const CombineParams p) {
   const int lane = threadIdx.x & 63;
@@ -48,24 +48,56 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineParams p) {
     for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
     total = m + logf(z);
   }
-  for (int d = 4 * lane; d < p.dv; d += 256) {
+  const bool live = total != -__builtin_inff();
+  // output columns: lane covers 4 columns per pass of 256
+  const int npass = (p.dv + 255) / 256;
+  const float *orow = p.o_part + r * p.dv;
+  const long long work_stride = rpb * p.dv;  // elements between the same row of consecutive works
+  for (int d = 4 * lane, pass = 0; pass < npass; d += 256, ++pass) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (total != -__builtin_inff()) {
-      for (int s = 0; s < count; ++s) {
-        const long long pr = (long long)(start + s) * rpb + r;
-        const float ls = p.lse_part[pr];
-        if (ls == -__builtin_inff()) continue;
-        const float wgt = expf(ls - total);
-        acc += wgt * *reinterpret_cast<const f32x4 *>(p.o_part + pr * p.dv + d);
+    // every lane runs the loop (the weights move between lanes); a lane past
+    // the last column reads the last four and stores nothing
+    const int dd = min(d, p.dv - 4);
+    if (live) {
+      // works in groups of 64: lane s of the wave holds the weight of work
+      // g0 + s; the loads of one group are independent and issue 4 at a time
+      for (int g0 = 0; g0 < count; g0 += 64) {
+        const int ng = min(64, count - g0);
+        float wl = 0.f;
+        if (lane < ng) {
+          const float ls = p.lse_part[(long long)(start + g0 + lane) * rpb + r];
+          wl = ls == -__builtin_inff() ? 0.f : expf(ls - total);
+        }
+        const float *base = orow + (long long)(start + g0) * work_stride + dd;
+        // a work of weight 0 (LSE -inf, or negligible) is skipped, whatever
+        // its partial holds
+        auto add = [&](int s, const f32x4 &v) {
+          const float wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s));
+          if (wgt != 0.f) acc += wgt * v;
+        };
+        int s = 0;
+        for (; s + 4 <= ng; s += 4) {
+          const f32x4 v0 = *reinterpret_cast<const f32x4 *>(base + (long long)s * work_stride);
+          const f32x4 v1 = *reinterpret_cast<const f32x4 *>(base + (long long)(s + 1) * work_stride);
+          const f32x4 v2 = *reinterpret_cast<const f32x4 *>(base + (long long)(s + 2) * work_stride);
+          const f32x4 v3 = *reinterpret_cast<const f32x4 *>(base + (long long)(s + 3) * work_stride);
+          add(s, v0);
+          add(s + 1, v1);
+          add(s + 2, v2);
+          add(s + 3, v3);
+        }
+        for (; s < ng; ++s) add(s, *reinterpret_cast<const f32x4 *>(base + (long long)s * work_stride));
       }
     }
-    if (p.out_bf16) {
-      bf16x4 o;
+    if (d < p.dv) {
+      if (p.out_bf16) {
+        bf16x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = static_cast<__bf16>(acc[i]);
-      *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(p.out) + row * p.dv + d) = o;
-    } else {
-      *reinterpret_cast<f32x4 *>(static_cast<float *>(p.out) + row * p.dv + d) = acc;
+        for (int i = 0; i < 4; ++i) o[i] = static_cast<__bf16>(acc[i]);
+        *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(p.out) + row * p.dv + d) = o;
+      } else {
+        *reinterpret_cast<f32x4 *>(static_cast<float *>(p.out) + row * p.dv + d) = acc;
+      }
     }
   }
   if (p.lse && lane == 0) p.lse[row] = total;
