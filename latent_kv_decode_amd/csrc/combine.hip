@@ -8,8 +8,9 @@
 // computation only as one softmax over the whole cache, and the merge follows
 // from writing that softmax over a partition of the cache.
 //
-// One wave per (b, t, h) row; lanes stride over the value columns in float4,
-// and the weights of up to 64 works sit one per lane.
+// One wave per (b, t, h) row; lanes stride over the value columns in float4.
+// A row with at most 4 works loads all its partials at once; with more, the
+// weights of up to 64 works sit one per lane and the loads go 4 at a time.
 #include "lkv_internal.h"
 
 namespace lkv {
@@ -17,6 +18,66 @@ namespace {
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+
+__device__ __forceinline__ void store4(const CombineParams &p, long long at, const f32x4 &v) {
+  if (p.out_bf16) {
+    bf16x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = static_cast<__bf16>(v[i]);
+    *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(p.out) + at) = o;
+  } else {
+    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.out) + at) = v;
+  }
+}
+
+// A row with N (1..4) works: every lane loads its columns of all N partials
+// at once (up to 4 passes of 256 columns), then weighs and sums them.
+template <int N>
+__device__ __forceinline__ void combine_few(const CombineParams &p, long long row, long long r, int start,
+                                            int lane) {
+  const long long rpb = (long long)p.s_q * p.h_q;
+  float ls[N], wgt[N];
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int s = 0; s < N; ++s) {
+    ls[s] = p.lse_part[(long long)(start + s) * rpb + r];
+    m = fmaxf(m, ls[s]);
+  }
+  float total = -__builtin_inff();
+  if (m != -__builtin_inff()) {
+    float z = 0.f;
+#pragma unroll
+    for (int s = 0; s < N; ++s) z += expf(ls[s] - m);
+    total = m + logf(z);
+  }
+#pragma unroll
+  for (int s = 0; s < N; ++s)
+    wgt[s] = total == -__builtin_inff() || ls[s] == -__builtin_inff() ? 0.f : expf(ls[s] - total);
+  const float *base = p.o_part + ((long long)start * rpb + r) * p.dv;
+  const long long work_stride = rpb * p.dv;
+  f32x4 v[4][N];
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int d = 4 * lane + 256 * pass;
+    if (d < p.dv) {
+#pragma unroll
+      for (int s = 0; s < N; ++s) v[pass][s] = *reinterpret_cast<const f32x4 *>(base + s * work_stride + d);
+    }
+  }
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int d = 4 * lane + 256 * pass;
+    if (d < p.dv) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      // a work of weight 0 is skipped, whatever its partial holds
+#pragma unroll
+      for (int s = 0; s < N; ++s)
+        if (wgt[s] != 0.f) acc += wgt[s] * v[pass][s];
+      store4(p, row * p.dv + d, acc);
+    }
+  }
+  if (p.lse && lane == 0) p.lse[row] = total;
+}
 
 __global__ void __launch_bounds__(256) combine_kernel(const CombineParams p) {
   const int lane = threadIdx.x & 63;
@@ -34,6 +95,13 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineParams p) {
     count = p.meta[2 * b + 1];
   }
   if (p.skip_single && count <= 1) return;
+  switch (count) {
+    case 1: combine_few<1>(p, row, r, start, lane); return;
+    case 2: combine_few<2>(p, row, r, start, lane); return;
+    case 3: combine_few<3>(p, row, r, start, lane); return;
+    case 4: combine_few<4>(p, row, r, start, lane); return;
+    default: break;
+  }
 
   // maximum LSE over the works (lanes stride over works)
   float m = -__builtin_inff();
@@ -89,16 +157,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineParams p) {
         for (; s < ng; ++s) add(s, *reinterpret_cast<const f32x4 *>(base + (long long)s * work_stride));
       }
     }
-    if (d < p.dv) {
-      if (p.out_bf16) {
-        bf16x4 o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = static_cast<__bf16>(acc[i]);
-        *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(p.out) + row * p.dv + d) = o;
-      } else {
-        *reinterpret_cast<f32x4 *>(static_cast<float *>(p.out) + row * p.dv + d) = acc;
-      }
-    }
+    if (d < p.dv) store4(p, row * p.dv + d, acc);
   }
   if (p.lse && lane == 0) p.lse[row] = total;
 }

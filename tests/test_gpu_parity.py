@@ -90,6 +90,47 @@ def test_mla_split_plans_agree(lkv, oracle):
         assert np.abs(o - outs[0]).max() < 2e-2
 
 
+def _shares(seqlens, splits):
+    """Shares each sequence is cut into when the concatenated 64-token tiles
+    of the batch (an empty sequence counts one tile) are cut into `splits`
+    equal shares."""
+    tiles = [max(1, -(-int(L) // 64)) for L in seqlens]
+    chunk = -(-sum(tiles) // splits)
+    out, cu = [], 0
+    for nb in tiles:
+        out.append((cu + nb - 1) // chunk - cu // chunk + 1)
+        cu += nb
+    return out
+
+
+def test_mla_split_share_counts(lkv, oracle):
+    """128 query rows per latent head, with plans that cut the sequences into
+    1, 2, 3, 4 and more shares (an empty sequence among them).  Every plan
+    runs with and without host lengths (with them the combine pass is skipped
+    when no sequence is cut), twice in a row on the same workspace, into
+    outputs poisoned with NaN so that a row left unwritten fails."""
+    seqlens = [2000, 130, 700, 64, 5, 1500, 300, 1, 2600, 190]
+    w, x = small_mla(260, B=len(seqlens), seqlens=seqlens)
+    x["seqlens"][4] = 0
+    d = mla_device_inputs(x, w, torch)
+    ro, rl = oracle_mla(oracle, w, x)
+    seen = set()
+    for splits in (5, 9, 16, 23, 64):
+        shares = _shares(x["seqlens"], splits)
+        seen.update(shares)
+        for host in (True, False):
+            for rep in range(2):
+                note(f"case share counts splits={splits} shares={shares} host={host} rep={rep}")
+                out = torch.full((w.B, 1, w.h_q, w.d_c), float("nan"), dtype=torch.bfloat16,
+                                 device="cuda")
+                lse = torch.full((w.B, 1, w.h_q), float("nan"), dtype=torch.float32, device="cuda")
+                out, lse = run_mla(lkv, w, d, x=x if host else None, num_splits=splits, out=out,
+                                   lse=lse)
+                assert_close(from_dev(out), ro, from_dev(lse), rl,
+                             what=f"splits={splits} host={host} rep={rep}")
+    assert {1, 2, 3, 4} <= seen and max(seen) > 4, seen
+
+
 @pytest.mark.parametrize("h_q,n_lat,d_c", [(32, 2, 256), (16, 1, 512), (64, 1, 128), (48, 1, 512)])
 def test_mla_head_shapes(lkv, oracle, h_q, n_lat, d_c):
     """GLA-2 (two latent heads, shared RoPE key), few heads (one 16-row tile),
