@@ -15,11 +15,13 @@ the split-KV combine).  Other workloads (lkv_inputs.WORKLOADS):
                                8 key/value groups once (timed separately, not
                                part of the step), then grouped decode
 
-Timing: W untimed warm-up steps, then K timed steps bracketed by device
-synchronisation.  One pair of HIP events on the stream the library launches
+Timing: W untimed warm-up steps (default 150: the first ~100 steps of a run
+are up to 20% slower while the chip settles), then K timed steps bracketed by
+device synchronisation.  One pair of HIP events on the stream the library launches
 on brackets the K steps (the step time is their span over K), and a pair per
-step, recorded by the library itself around the attention kernel
-(kernel_events), times that kernel alone for the roofline.  Four
+step, attached by the library to the attention kernel's own launch
+(kernel_events, no marker packets between kernels), times that kernel alone
+for the roofline.  Four
 independent copies of the cache rotate from step to step so that the 256 MB
 Infinity Cache cannot hold the working set.
 
@@ -76,7 +78,7 @@ def measured_traffic(workload: str):
 
 class HipEvents:
     """Raw hipEvent_t handles through the HIP runtime (ctypes): the library
-    records them on its own launch stream around the attention kernel."""
+    attaches them to the attention kernel's launch on its own stream."""
 
     def __init__(self):
         import ctypes
@@ -345,7 +347,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # the chip settles about 100 steps (10-20 ms) into a run of the headline
+    # shape; a shorter warm-up times part of that transient
+    ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--workload", default="dsv3_mla_b64_l4096")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -396,6 +400,16 @@ def main():
     wall = time.perf_counter() - t0
     span = e_start.elapsed_time(e_end) * 1e-3  # seconds, K steps
     kern = np.array([hip.elapsed_ms(a, b) for a, b in kev]) * 1e-3
+    # the spread of single steps, from a second (untimed) pass with an event
+    # pair per step; events between steps add their own small gaps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)]) * 1e-3
     for a, b in kev:
         hip.destroy(a)
         hip.destroy(b)
@@ -435,6 +449,8 @@ def main():
                                      float(np.percentile(kern, 10) * 1e6),
                                      float(np.percentile(kern, 90) * 1e6)],
         "step_us": t_step * 1e6,
+        "step_us_median_p10_p90_single": [float(np.median(per) * 1e6), float(np.percentile(per, 10) * 1e6),
+                                          float(np.percentile(per, 90) * 1e6)],
         "algorithmic": {"bytes_per_launch": work.bytes, "flops_per_launch": work.flops,
                         "intensity": work.intensity},
         "parity_sample_rel_l2": rel,

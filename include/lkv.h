@@ -120,9 +120,11 @@ const char *lkv_last_error(void);
  *   seqlens_host  host int32 [batch] copy of seqlens, or NULL.  Used only to
  *           skip the combine pass when no sequence is split; it must then
  *           equal the device values.
- *   kernel_events  optional pair of hipEvent_t (either may be NULL): recorded
- *           on `stream` immediately before and after the attention kernel
- *           (not the combine pass), for timing that kernel alone.
+ *   kernel_events  optional pair of hipEvent_t (either may be NULL), for
+ *           timing the attention kernel alone (not the combine pass): they
+ *           are attached to that kernel's launch (hipExtLaunchKernel) and
+ *           take its start and end times, with no marker packet added to
+ *           the stream.  Not recorded when the batch is empty.
  * Supported: bf16 with (d_c, d_rope) in {(512, 64), (256, 64), (128, 64),
  *   (512, 0)}, and also (256, 0) when a latent head has more than 32 query
  *   rows ((h_q / n_latent) * s_q > 32); f32 with d_c + d_rope <= 1024.  Any

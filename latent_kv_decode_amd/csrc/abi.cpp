@@ -94,7 +94,12 @@ lkv_status make_plan(const Shape &s, Plan *pl) {
   int cus = 0;
   if (device_cus(&cus) != 0) return fail(LKV_ERR_HIP, "cannot query the device compute-unit count");
   const int groups = s.n_kvh * pl->row_tiles;
-  int chunks = s.num_splits > 0 ? s.num_splits : std::max(1, cus / std::max(1, groups));
+  // automatic plan: one share per row group for every work-group slot of the
+  // chip (CUs x work-groups resident per CU)
+  int per_cu = 1;
+  if (s.dtype == LKV_BF16 && pl->latent == kLatentNone)
+    per_cu = lkv::mfma_decode_blocks_per_cu(s.dk, s.dr, s.dv, s.v_alias, pl->rows);
+  int chunks = s.num_splits > 0 ? s.num_splits : std::max(1, cus * per_cu / std::max(1, groups));
   chunks = std::min(chunks, 1 << 20);
   pl->n_chunks = chunks;
   const size_t slots = (size_t)s.B + (size_t)chunks;
@@ -228,27 +233,22 @@ lkv_status run_decode(const Shape &s, const Ptrs &p, float scale) {
   d.dr = s.dr;
   d.dv = s.dv;
 
+  lkv::LaunchEvents ev;
+  ev.start = static_cast<hipEvent_t>(p.events[0]);
+  ev.stop = static_cast<hipEvent_t>(p.events[1]);
   hipError_t e;
   if (s.dtype == LKV_F32) {
-    if (p.events[0] && (e = hipEventRecord(static_cast<hipEvent_t>(p.events[0]), p.stream)) != hipSuccess)
-      return hip_fail(e, "kernel_events[0] record");
-    e = lkv::launch_f32_decode(d, p.stream);
+    e = lkv::launch_f32_decode(d, p.stream, ev);
     if (e != hipSuccess) return hip_fail(e, "float32 decode launch");
-    if (p.events[1] && (e = hipEventRecord(static_cast<hipEvent_t>(p.events[1]), p.stream)) != hipSuccess)
-      return hip_fail(e, "kernel_events[1] record");
     return LKV_OK;
   }
   char *ws = static_cast<char *>(p.ws);
   d.o_part = reinterpret_cast<float *>(ws);
   d.lse_part = reinterpret_cast<float *>(ws + pl.ws_opart);
   d.meta = reinterpret_cast<int32_t *>(ws + pl.ws_opart + pl.ws_lse);
-  if (p.events[0] && (e = hipEventRecord(static_cast<hipEvent_t>(p.events[0]), p.stream)) != hipSuccess)
-    return hip_fail(e, "kernel_events[0] record");
-  e = pl.latent == kLatentSplit ? lkv::launch_mla_split(d, p.stream)
-                                : lkv::launch_mfma_decode(d, s.v_alias, pl.rows, p.stream);
+  e = pl.latent == kLatentSplit ? lkv::launch_mla_split(d, p.stream, ev)
+                                : lkv::launch_mfma_decode(d, s.v_alias, pl.rows, p.stream, ev);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  if (p.events[1] && (e = hipEventRecord(static_cast<hipEvent_t>(p.events[1]), p.stream)) != hipSuccess)
-    return hip_fail(e, "kernel_events[1] record");
   if (p.seqlens_host && !any_split(p.seqlens_host, s.B, pl.n_chunks)) return LKV_OK;
   lkv::CombineParams c{};
   c.o_part = d.o_part;

@@ -97,11 +97,10 @@ __global__ void __launch_bounds__(256) f32_decode_kernel(const DecodeParams p) {
 
 }  // namespace
 
-hipError_t launch_f32_decode(const DecodeParams &p, hipStream_t s) {
+hipError_t launch_f32_decode(const DecodeParams &p, hipStream_t s, const LaunchEvents &ev) {
   const long long rows = (long long)p.B * p.s_q * p.h_q;
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(f32_decode_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_timed(f32_decode_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), s, ev, p);
 }
 
 }  // namespace lkv

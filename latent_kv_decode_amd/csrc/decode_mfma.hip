@@ -629,16 +629,31 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
 }
 
 template <int DK, int DR, int DV, bool VA, int ROWS>
-hipError_t launch(const DecodeParams &p, hipStream_t s) {
+hipError_t launch(const DecodeParams &p, hipStream_t s, const LaunchEvents &ev) {
   const int G = p.n_kvh * p.row_tiles;
   const int cpad = (p.n_chunks + 7) / 8 * 8;
-  hipLaunchKernelGGL((mfma_decode_kernel<DK, DR, DV, VA, ROWS>), dim3(G * cpad), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+  return launch_timed(mfma_decode_kernel<DK, DR, DV, VA, ROWS>, dim3(G * cpad), dim3(kThreads), s, ev, p);
 }
 
 template <int DK, int DR, int DV, bool VA>
-hipError_t launch_rows(const DecodeParams &p, int rows, hipStream_t s) {
-  return rows == 16 ? launch<DK, DR, DV, VA, 16>(p, s) : launch<DK, DR, DV, VA, 32>(p, s);
+hipError_t launch_rows(const DecodeParams &p, int rows, hipStream_t s, const LaunchEvents &ev) {
+  return rows == 16 ? launch<DK, DR, DV, VA, 16>(p, s, ev) : launch<DK, DR, DV, VA, 32>(p, s, ev);
+}
+
+// Work-groups of one instantiation resident on a CU at once (registers and
+// LDS), queried once per instantiation; 1 if the query fails.
+template <int DK, int DR, int DV, bool VA, int ROWS>
+int blocks_per_cu() {
+  static int cached = 0;  // the same for every gfx950 device
+  if (cached == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mfma_decode_kernel<DK, DR, DV, VA, ROWS>, kThreads, 0) !=
+            hipSuccess ||
+        n < 1)
+      n = 1;
+    cached = n;
+  }
+  return cached;
 }
 
 }  // namespace
@@ -664,9 +679,19 @@ bool mfma_decode_supported(int dk, int dr, int dv, bool v_alias, int) {
   return false;
 }
 
-hipError_t launch_mfma_decode(const DecodeParams &p, bool v_alias, int rows, hipStream_t s) {
+int mfma_decode_blocks_per_cu(int dk, int dr, int dv, bool v_alias, int rows) {
+#define LKV_OCC(DK, DR, DV, VA)                                   \
+  if (dk == DK && dr == DR && dv == DV && v_alias == VA)          \
+    return rows == 16 ? blocks_per_cu<DK, DR, DV, VA, 16>() : blocks_per_cu<DK, DR, DV, VA, 32>();
+  LKV_MFMA_VARIANTS(LKV_OCC)
+#undef LKV_OCC
+  return 1;
+}
+
+hipError_t launch_mfma_decode(const DecodeParams &p, bool v_alias, int rows, hipStream_t s,
+                              const LaunchEvents &ev) {
 #define LKV_DISPATCH(DK, DR, DV, VA) \
-  if (p.dk == DK && p.dr == DR && p.dv == DV && v_alias == VA) return launch_rows<DK, DR, DV, VA>(p, rows, s);
+  if (p.dk == DK && p.dr == DR && p.dv == DV && v_alias == VA) return launch_rows<DK, DR, DV, VA>(p, rows, s, ev);
   LKV_MFMA_VARIANTS(LKV_DISPATCH)
 #undef LKV_DISPATCH
   return hipErrorInvalidValue;

@@ -654,11 +654,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
 }
 
 template <int DK, int DR>
-hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
+hipError_t launch_split(const DecodeParams &p, hipStream_t s, const LaunchEvents &ev) {
   const int G = p.n_kvh * p.row_tiles;
   const int cpad = (p.n_chunks + 7) / 8 * 8;
-  hipLaunchKernelGGL((mla_split_kernel<DK, DR>), dim3(G * cpad), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+  return launch_timed(mla_split_kernel<DK, DR>, dim3(G * cpad), dim3(kThreads), s, ev, p);
 }
 
 }  // namespace
@@ -667,11 +666,11 @@ bool mla_split_supported(int dk, int dr) { return (dk == 512 || dk == 256) && (d
 
 int mla_split_rows() { return kRows; }
 
-hipError_t launch_mla_split(const DecodeParams &p, hipStream_t s) {
-  if (p.dk == 512 && p.dr == 64) return launch_split<512, 64>(p, s);
-  if (p.dk == 512 && p.dr == 0) return launch_split<512, 0>(p, s);
-  if (p.dk == 256 && p.dr == 64) return launch_split<256, 64>(p, s);
-  if (p.dk == 256 && p.dr == 0) return launch_split<256, 0>(p, s);
+hipError_t launch_mla_split(const DecodeParams &p, hipStream_t s, const LaunchEvents &ev) {
+  if (p.dk == 512 && p.dr == 64) return launch_split<512, 64>(p, s, ev);
+  if (p.dk == 512 && p.dr == 0) return launch_split<512, 0>(p, s, ev);
+  if (p.dk == 256 && p.dr == 64) return launch_split<256, 64>(p, s, ev);
+  if (p.dk == 256 && p.dr == 0) return launch_split<256, 0>(p, s, ev);
   return hipErrorInvalidValue;
 }
 

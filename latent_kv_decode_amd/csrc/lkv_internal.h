@@ -2,10 +2,27 @@
 // C ABI (abi.cpp) and the HIP kernel files.  Not part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace lkv {
+
+// Timing events attached to one kernel launch (either may be null): the
+// runtime stamps them with that dispatch's own start and end times, so no
+// marker packet enters the stream.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename K, typename... A>
+inline hipError_t launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t s, const LaunchEvents &ev, A... args) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  return hipGetLastError();
+}
 
 // Cache tokens per tile: the unit of work of the decode kernels and of the
 // split-KV planner.
@@ -66,13 +83,17 @@ struct ExpandParams {
 // matches (the ABI checks support before calling).
 bool mfma_decode_supported(int dk, int dr, int dv, bool v_alias, int rows_per_kvh);
 int mfma_decode_rows(int rows_per_kvh);  // ROWS template used for this problem
-hipError_t launch_mfma_decode(const DecodeParams &p, bool v_alias, int rows, hipStream_t s);
+// Work-groups of the instantiation for (dk, dr, dv, v_alias, rows) that fit
+// on one CU at once.
+int mfma_decode_blocks_per_cu(int dk, int dr, int dv, bool v_alias, int rows);
+hipError_t launch_mfma_decode(const DecodeParams &p, bool v_alias, int rows, hipStream_t s,
+                              const LaunchEvents &ev);
 // Latent path with the score and value products on different waves, 64 query
 // rows per work-group (decode_split.hip).
 bool mla_split_supported(int dk, int dr);
 int mla_split_rows();
-hipError_t launch_mla_split(const DecodeParams &p, hipStream_t s);
-hipError_t launch_f32_decode(const DecodeParams &p, hipStream_t s);
+hipError_t launch_mla_split(const DecodeParams &p, hipStream_t s, const LaunchEvents &ev);
+hipError_t launch_f32_decode(const DecodeParams &p, hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_combine(const CombineParams &p, hipStream_t s);
 bool expand_supported(int d_c, int d_h);
 hipError_t launch_expand(const ExpandParams &p, hipStream_t s);
