@@ -238,14 +238,17 @@ struct Cfg {
   static constexpr int KW = DK + DR;
   static_assert(DK % 64 == 0 && DR % 64 == 0 && DV % 64 == 0, "widths must be multiples of 64");
   static_assert(!VA || DV == DK, "the latent is the value");
-  // LDS tile buffer: key main part [64][DK], RoPE key [64][DR], and for
-  // separate values [64][DV]; every region row is a multiple of 128 bytes.
-  static constexpr int ROFF = kTile * DK;                // RoPE region offset (elements)
-  static constexpr int VOFF = ROFF + kTile * DR;         // value region offset
+  // LDS tile buffer: key main part [64][DK] and, for separate values,
+  // [64][DV]; every region row is a multiple of 128 bytes.  The RoPE key
+  // fragments go from memory straight to registers (each lane's share of
+  // them is one contiguous 16-byte piece per k-step), which keeps the
+  // buffers small enough for two work-groups per CU where that matters.
+  static constexpr int VOFF = kTile * DK;                // value region offset
   static constexpr int VSTR = DV;
   static constexpr int BUF = VOFF + (VA ? 0 : kTile * DV);
   static constexpr int KS = KW / 32;                     // k-steps of QK^T
   static constexpr int KSN = DK / 32;                    // of which on the main part
+  static constexpr int KSR = DR / 32;                    // and on the RoPE key
   static constexpr int NT = ROWS / 16;
   static constexpr int DVW = DV / kWaves;
   static constexpr int MT = DVW / 16;
@@ -291,26 +294,20 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
   const bool aligned_pages = p.page_shift >= 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   ContigDma<DK / 8> dk_;
-  ContigDma<(DR > 0 ? DR : 64) / 8> dr_;
   ContigDma<DV / 8> dv_;
   dk_.init(p.k_stride, wu, lane);
-  if constexpr (DR > 0) dr_.init(p.r_stride, wu, lane);
   if constexpr (!VA) dv_.init(p.v_stride, wu, lane);
 
   // Per-lane LDS element offsets of the fragment reads; the rest of each
   // address is a compile-time immediate.
   //  key (QK^T A operand): row tok = 16w + n, chunk 4ks + g.  The swizzle
   //    changes the low four chunk bits only, so the slot is
-  //    16*(ks/4) + ((4*(ks%4) + g) ^ h(tok)) for the main part and
-  //    (4*(ks%2) + g) ^ h8(tok) for the 8-chunk RoPE rows.
-  int koff[4], roff[2];
+  //    16*(ks/4) + ((4*(ks%4) + g) ^ h(tok)).
+  int koff[4];
   {
     const int tok = 16 * w + n;
 #pragma unroll
     for (int e = 0; e < 4; ++e) koff[e] = tok * DK + swz<DK / 8>(4 * e + g, tok) * 8;
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-      roff[e] = DR > 0 ? tok * DR + swz<(DR > 0 ? DR : 64) / 8>(4 * e + g, tok) * 8 : 0;
   }
   //  value (transpose read): rows rv = 8g + n/4 (+4), value column block mt of
   //    this wave -> chunk w*DVW/8 + 2mt + (n%4)/2, element (n%2)*4
@@ -400,11 +397,23 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
       if (lo < win || hi >= win + 64) {
         win = lo;
         btw = win + lane < npages ? bt[win + lane] : -1;
+        // wait here, on the refill path only: the compiler would otherwise
+        // wait at the join after this branch, on every tile
+        wait_vmem();
       }
     };
     const int row_first = L > 0 ? bt[0] * p.page_size : 0;
 
-    auto load_tile = [&](int tile, bf16 *buf) {
+    // RoPE key fragments (QK^T A operand, k-steps KSN..KS-1) of this lane's
+    // token 16w + n: the current tile's and the next one's
+    bf16x8 rcur[C::KSR > 0 ? C::KSR : 1], rnxt[C::KSR > 0 ? C::KSR : 1];
+    auto load_rope = [&](long long row, bf16x8 *dst) {
+#pragma unroll
+      for (int e = 0; e < C::KSR; ++e)
+        dst[e] = *reinterpret_cast<const bf16x8 *>(rc + row * p.r_stride + 32 * e + 8 * g);
+    };
+
+    auto load_tile = [&](int tile, bf16 *buf, bf16x8 *rdst) {
       const int jb = tile * kTile;
       if (aligned_pages && jb + kTile <= L) {
         // whole tile valid and inside one page: token t sits at row row0 + t
@@ -413,8 +422,8 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
         const int pg = __builtin_amdgcn_readlane(btw, pi - win);
         const long long row0 = (long long)pg * p.page_size + (jb & (p.page_size - 1));
         dk_.issue(kc + row0 * p.k_stride, p.k_stride, buf, wu);
-        if constexpr (DR > 0) dr_.issue(rc + row0 * p.r_stride, p.r_stride, buf + C::ROFF, wu);
         if constexpr (!VA) dv_.issue(vc + row0 * p.v_stride, p.v_stride, buf + C::VOFF, wu);
+        if constexpr (DR > 0) load_rope(row0 + 16 * w + n, rdst);
       } else {
         // general path: lane t computes the row of token t; tokens past the
         // sequence read token 0's row (valid, finite; their weight is 0)
@@ -423,8 +432,8 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
         const int pg = __shfl(btw, (page_of(j) - win) & 63);
         const int rr = j < L ? pg * p.page_size + slot_of(j) : row_first;
         dma_region<DK / 8>(kc, p.k_stride, buf, rr, w, lane);
-        if constexpr (DR > 0) dma_region<DR / 8>(rc, p.r_stride, buf + C::ROFF, rr, w, lane);
         if constexpr (!VA) dma_region<DV / 8>(vc, p.v_stride, buf + C::VOFF, rr, w, lane);
+        if constexpr (DR > 0) load_rope(__shfl(rr, 16 * w + n), rdst);
       }
     };
 
@@ -432,9 +441,11 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
     // wait for them is left inside the tile loop (where it would drain the
     // prefetch of the next tile as well).
     if (L > 0) {
-      load_tile(lt0, s_buf0);
+      load_tile(lt0, s_buf0, rcur);
       wait_vmem();
     } else {
+#pragma unroll
+      for (int e = 0; e < C::KSR; ++e) rcur[e] = bf16x8{};
       wait_vmem();
       // empty sequence: one all-masked tile of zeros
       for (int i = tid; i < C::BUF / 8; i += kThreads)
@@ -458,7 +469,7 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
       bf16 *const kt = BI == 0 ? s_buf0 : s_buf1;
       bf16 *const nxt = BI == 0 ? s_buf1 : s_buf0;
       const bool has_next = it + 1 < lt1;
-      if (has_next) load_tile(it + 1, nxt);
+      if (has_next) load_tile(it + 1, nxt, rnxt);
 
       // ---- S^T = K Q^T for tokens 16w..16w+15; every key fragment is read
       // before the first MFMA so the LDS latency is paid once per tile
@@ -470,9 +481,10 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           // chunk 4ks + g of row tok: slot 8(ks/2) + ((4(ks%2) + g) ^ sig)
-          const bf16 *src = ks < C::KSN ? kt + koff[ks & 3] + 128 * (ks >> 2)
-                                        : kt + C::ROFF + roff[(ks - C::KSN) & 1];
-          kf[ks] = *reinterpret_cast<const bf16x8 *>(src);
+          if (ks < C::KSN)
+            kf[ks] = *reinterpret_cast<const bf16x8 *>(kt + koff[ks & 3] + 128 * (ks >> 2));
+          else
+            kf[ks] = rcur[ks - C::KSN];
         }
         __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, KS * NT, 0);
@@ -575,6 +587,8 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
       // compiler assuming a load may still be in flight into the next step
       wait_vmem();
       __syncthreads();
+#pragma unroll
+      for (int e = 0; e < C::KSR; ++e) rcur[e] = rnxt[e];
     };
     for (int it = lt0; it < lt1; it += 2) {
       step(std::integral_constant<int, 0>{}, it);
