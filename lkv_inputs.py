@@ -15,7 +15,10 @@ Workloads mirror the shapes the pages model:
     technical summary sections 2-3;
   * plain GQA vs GLA-2 (two latent heads), the GTA/GLA article's GLA
     section; and a long-context ragged batch (1K-64K, the article's decode
-    range).
+    range);
+  * variants on the same kernels: GQLA with g = 4 and s_q = 1, four query
+    tokens per step (multi-token prediction), GTA's tied key/value groups
+    and GQA-2 with 64 query heads per KV head (VHA's inference form).
 Draw order inside one seed: seqlens, block table, q_nope (or q), q_rope,
 c_kv (or K then V), k_rope, W_UK, W_UV.
 """
@@ -209,6 +212,29 @@ WORKLOADS = {
                              s_q=2, page_size=64, n_lat=1, d_c=512, d_rope=64,
                              seqlen_range=(1024, 65536), table="fragmented", max_pages=1024,
                              scale=1 / math.sqrt(576), seed=5),
+    # variants on the same kernels
+    # GQLA grouped path with g = 4 groups and one query token (the GQLA
+    # explainer's other grouped setting)
+    "gqla_g4_b64_l4096_sq1": _w(name="gqla_g4_b64_l4096_sq1", kind="gqla", dtype="bf16", B=64,
+                                h_q=128, s_q=1, page_size=64, n_lat=1, d_c=512, n_kv=4, d_h=128,
+                                d_rope=64, seqlens=(4096,) * 64, table="shuffled",
+                                scale=1 / math.sqrt(192), seed=6),
+    # multi-token prediction: four query tokens per step on the MLA path
+    "mtp_mla_b64_l4096_sq4": _w(name="mtp_mla_b64_l4096_sq4", kind="mla", dtype="bf16", B=64,
+                                h_q=128, s_q=4, page_size=64, n_lat=1, d_c=512, d_rope=64,
+                                seqlens=(4096,) * 64, table="shuffled",
+                                scale=1 / math.sqrt(576), seed=7),
+    # GTA (grouped-tied attention): 8 groups whose key and value are one
+    # tied 128-wide state, plus a shared 64-wide RoPE key -- the absorbed
+    # layout with one latent head per group
+    "gta_b128_l8192": _w(name="gta_b128_l8192", kind="mla", dtype="bf16", B=128, h_q=32, s_q=1,
+                         page_size=64, n_lat=8, d_c=128, d_rope=64, seqlens=(8192,) * 128,
+                         table="shuffled", scale=1 / math.sqrt(192), seed=8),
+    # GQA-2 (two KV heads, 64 query heads each), the inference form of VHA
+    "vha_gqa2_b64_l8192": _w(name="vha_gqa2_b64_l8192", kind="gqa", dtype="bf16", B=64, h_q=128,
+                             s_q=1, page_size=64, n_kv=2, d_h=128, d_rope=0,
+                             seqlens=(8192,) * 64, table="shuffled", scale=1 / math.sqrt(128),
+                             seed=9),
 }
 
 

@@ -131,10 +131,12 @@ def test_mla_split_share_counts(lkv, oracle):
     assert {1, 2, 3, 4} <= seen and max(seen) > 4, seen
 
 
-@pytest.mark.parametrize("h_q,n_lat,d_c", [(32, 2, 256), (16, 1, 512), (64, 1, 128), (48, 1, 512)])
+@pytest.mark.parametrize("h_q,n_lat,d_c", [(32, 2, 256), (16, 1, 512), (64, 1, 128), (48, 1, 512),
+                                          (32, 8, 128)])
 def test_mla_head_shapes(lkv, oracle, h_q, n_lat, d_c):
     """GLA-2 (two latent heads, shared RoPE key), few heads (one 16-row tile),
-    a narrow latent, and a head count that leaves a padded row tile."""
+    a narrow latent, a head count that leaves a padded row tile, and GTA
+    (eight tied key/value groups of 128 as latent heads, shared RoPE key)."""
     w, x = small_mla(300 + h_q, B=3, h_q=h_q, n_lat=n_lat, d_c=d_c, seqlens=[77, 300, 129])
     note(f"case mla_heads h_q={h_q} n_lat={n_lat} d_c={d_c}")
     d = mla_device_inputs(x, w, torch)
@@ -145,7 +147,7 @@ def test_mla_head_shapes(lkv, oracle, h_q, n_lat, d_c):
 
 @pytest.mark.parametrize("h_q,d_c,d_rope,s_q,splits", [
     (64, 256, 64, 1, 0), (128, 512, 0, 1, 0), (64, 256, 0, 2, 3), (128, 512, 64, 2, 0),
-    (96, 512, 64, 1, 5)])
+    (96, 512, 64, 1, 5), (128, 512, 64, 4, 0)])
 def test_mla_many_rows_widths(lkv, oracle, h_q, d_c, d_rope, s_q, splits):
     """Latent and RoPE widths (512/256, with and without RoPE) with many query
     rows per latent head, including a row count that is not a multiple of
@@ -284,7 +286,10 @@ def _oracle_gqa(oracle, w, x, rows=None):
 
 @pytest.mark.parametrize("h_q,n_kv,d_h,d_rope,s_q,splits", [
     (32, 8, 128, 0, 1, 0), (128, 8, 128, 64, 2, 0), (128, 8, 128, 64, 2, 7), (64, 2, 64, 0, 1, 3),
-    (16, 16, 256, 0, 1, 0), (8, 1, 128, 0, 2, 0)])
+    (16, 16, 256, 0, 1, 0), (8, 1, 128, 0, 2, 0),
+    # GQLA g = 4, s_q = 1; four query tokens (MTP) on g = 8; GQA-2 with 64
+    # query heads per KV head (VHA)
+    (128, 4, 128, 64, 1, 0), (128, 8, 128, 64, 4, 0), (128, 2, 128, 0, 1, 0)])
 def test_gqa_small(lkv, oracle, h_q, n_kv, d_h, d_rope, s_q, splits):
     w, x = _gqa_small(600 + h_q + d_h, h_q=h_q, n_kv=n_kv, d_h=d_h, d_rope=d_rope, s_q=s_q)
     note(f"case gqa h_q={h_q} n_kv={n_kv} d_h={d_h} d_rope={d_rope} s_q={s_q} splits={splits}")
@@ -411,7 +416,7 @@ def test_split_combine_entry_point(lkv, oracle):
 
 # ------------------------------------------------------- full-size workloads
 FULL = [("dsv3_mla_b64_l4096", 96), ("gla2_b128_l8192", 64), ("ragged_mla_b16_sq1", 48),
-        ("ragged_mla_b16_sq2", 48)]
+        ("ragged_mla_b16_sq2", 48), ("mtp_mla_b64_l4096_sq4", 64), ("gta_b128_l8192", 64)]
 
 
 @pytest.mark.parametrize("name,nrows", FULL)
@@ -431,9 +436,10 @@ def test_full_size_mla_sampled(lkv, oracle, name, nrows):
                  what=name)
 
 
-def test_full_size_gqa_sampled(lkv, oracle):
-    w = li.workload("gqa_b128_l8192")
-    note("case full gqa_b128_l8192: generating inputs")
+@pytest.mark.parametrize("name", ["gqa_b128_l8192", "vha_gqa2_b64_l8192"])
+def test_full_size_gqa_sampled(lkv, oracle, name):
+    w = li.workload(name)
+    note(f"case full {name}: generating inputs")
     x = li.generate(w)
     out, lse = _run_gqa(lkv, w, x)
     torch.cuda.synchronize()
@@ -442,12 +448,13 @@ def test_full_size_gqa_sampled(lkv, oracle):
     got, gl = from_dev(out), from_dev(lse)
     assert np.isfinite(got).all()
     assert_close(rows_of(got, rows), rows_of(ro, rows), rows_of(gl, rows), rows_of(rl, rows),
-                 what="gqa full")
+                 what=f"{name} full")
 
 
-def test_full_size_gqla_grouped_sampled(lkv, oracle):
-    w = li.workload("gqla_grouped_b64_l4096_sq2")
-    note("case full gqla: generating inputs")
+@pytest.mark.parametrize("name", ["gqla_grouped_b64_l4096_sq2", "gqla_g4_b64_l4096_sq1"])
+def test_full_size_gqla_grouped_sampled(lkv, oracle, name):
+    w = li.workload(name)
+    note(f"case full {name}: generating inputs")
     x = li.generate(w)
     kv, k_out, v_out = _expand_gpu(lkv, w, x)
     flat = kv.reshape(-1)
@@ -481,7 +488,7 @@ def test_full_size_gqla_grouped_sampled(lkv, oracle):
     q_h = li.bf16_bits_to_f32(x["q_nope_h"]).astype(np.float64)[seqs]
     q_r = li.bf16_bits_to_f32(x["q_rope"]).astype(np.float64)[seqs]
     sub_rows = np.array([seqs.index(int(r) // per) * per + int(r) % per for r in rows], np.int32)
-    note("case full gqla: oracle")
+    note(f"case full {name}: oracle")
     ro, rl = oracle.gqa_decode(q_h, np.nan_to_num(rk), np.nan_to_num(rv), sub_bt, sub_sl,
                                n_kv=w.n_kv, d_h=w.d_h, page_size=w.page_size, scale=w.scale,
                                q_rope=q_r, k_rope=np.nan_to_num(kr64), d_rope=w.d_rope,
@@ -489,4 +496,4 @@ def test_full_size_gqla_grouped_sampled(lkv, oracle):
     got, gl = from_dev(out), from_dev(lse)
     assert np.isfinite(got).all()
     assert_close(rows_of(got, rows), rows_of(ro, sub_rows), rows_of(gl, rows), rows_of(rl, sub_rows),
-                 what="gqla grouped full")
+                 what=f"{name} full")
