@@ -325,9 +325,18 @@ def _w64(x, k):
     return li.bf16_bits_to_f32(x[k]).astype(np.float64)
 
 
-def test_expand_matches_oracle(lkv, oracle):
-    w, x = _gqla_small(700)
-    note("case expand")
+@pytest.mark.parametrize("g,d_c,d_h,seqlens", [
+    (8, 512, 128, (130, 64)),
+    # three groups of 64 (a partial 256-column tile), one group of 256,
+    # sequences spanning several 256-token tiles with ragged ends
+    (3, 256, 64, (600, 257, 1)), (1, 128, 256, (300, 513))])
+def test_expand_matches_oracle(lkv, oracle, g, d_c, d_h, seqlens):
+    w = li.Workload(name="gqla", kind="gqla", dtype="bf16", B=len(seqlens), h_q=16 * g, s_q=1,
+                    page_size=64, n_lat=1, d_c=d_c, n_kv=g, d_h=d_h, d_rope=64,
+                    seqlens=tuple(seqlens), table="shuffled", scale=1 / math.sqrt(d_h + 64),
+                    seed=700 + g)
+    x = li.generate(w)
+    note(f"case expand g={g} d_c={d_c} d_h={d_h} seqlens={seqlens}")
     _, k_out, v_out = _expand_gpu(lkv, w, x)
     rk, rv = oracle.expand_latent(x["kv"].reshape(-1), _w64(x, "w_uk"), _w64(x, "w_uv"),
                                   x["block_table"], x["seqlens"], page_size=w.page_size,
