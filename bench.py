@@ -330,12 +330,55 @@ def setup_gqla(w, x, args, torch, lkv, rf):
 
     work = rf.gqa_work(x["seqlens"], s_q=w.s_q, h_q=w.h_q, n_kv=w.n_kv, d_h=w.d_h,
                        d_rope=w.d_rope, page_size=w.page_size, causal=w.causal)
+
+    # the steps on either side of absorbed decode, each timed on its own on
+    # the same weights (not part of the timed step): W_UK into the query,
+    # W_UV on the latent output, the step's new tokens into a copy of the
+    # latent cache
+    def timed_us(fn, n=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    q_h = to_dev(x["q_nope_h"], torch)
+    q_abs = lkv.lkv_absorb_query(q_h, wuk, stream=stream)
+    o_up = torch.empty_like(q_h)
+    kv_copy = kv.clone()
+    P = w.page_size
+    new_rows = torch.stack([torch.stack([kv[int(x["block_table"][b, j // P]), j % P]
+                                         for j in range(int(L) - w.s_q, int(L))])
+                            for b, L in enumerate(x["seqlens"])])
+    rows = w.B * w.s_q * w.h_q
+    wbytes = w.n_kv * w.d_c * w.d_h * 2
+    t_abs = timed_us(lambda: lkv.lkv_absorb_query(q_h, wuk, out=q_abs, stream=stream))
+    t_up = timed_us(lambda: lkv.lkv_up_project(q_abs, wuv, out=o_up, stream=stream))
+    t_app = timed_us(lambda: lkv.lkv_append_tokens(new_rows, kv_copy, bt, sl, page_size=P,
+                                                   stream=stream))
+    proj_flops = 2.0 * rows * w.d_c * w.d_h
+    proj_bytes = rows * (w.d_c + w.d_h) * 2 + wbytes
+    app_bytes = 2 * w.B * w.s_q * width * 2
+    del kv_copy
     n_tok = int(np.sum(x["seqlens"]))
     ew = rf.expand_work(n_tok, g=w.n_kv, d_c=w.d_c, d_h=w.d_h)
     extra = {"expansion": {"us": t_exp * 1e6, "tokens": n_tok, "algorithmic_bytes": ew.bytes,
                            "flops": ew.flops, "GB_per_s": ew.bytes / t_exp / 1e9,
                            "TFLOP_per_s": ew.flops / t_exp / 1e12,
-                           "note": "cache-write-time expansion, not part of the timed step"}}
+                           "note": "cache-write-time expansion, not part of the timed step"},
+             "absorb_query": {"us": t_abs, "flops": proj_flops, "bytes": proj_bytes,
+                              "GB_per_s": proj_bytes / t_abs / 1e3,
+                              "TFLOP_per_s": proj_flops / t_abs / 1e6},
+             "up_project": {"us": t_up, "flops": proj_flops, "bytes": proj_bytes,
+                            "GB_per_s": proj_bytes / t_up / 1e3,
+                            "TFLOP_per_s": proj_flops / t_up / 1e6},
+             "append_tokens": {"us": t_app, "bytes": app_bytes, "GB_per_s": app_bytes / t_app / 1e3,
+                               "note": "per step, B * s_q new rows of the latent + RoPE cache"}}
     return dict(step=step, work=work, parity=parity, cpu=cpu, kernel="mfma_decode_kernel",
                 extra=extra, config={"g": w.n_kv, "d_h": w.d_h, "d_rope": w.d_rope, "d_c": w.d_c})
 

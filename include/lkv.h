@@ -226,7 +226,7 @@ lkv_status lkv_gqa_decode_workspace_size(const lkv_gqa_args *args, size_t *bytes
  *   start_pos   device int32 [batch] or NULL (= 0): append-only expansion
  *   k_out, v_out  device bf16, element (row, g, e) at row*k_tok_stride + g*d_h + e
  *                 (v_tok_stride for v_out)
- * Supported: bf16, d_c a multiple of 64 up to 1024, d_h in {64, 128, 256}.
+ * Supported: bf16, d_c a multiple of 64 up to 512, d_h in {64, 128, 256}.
  * Rows outside [start_pos, seqlens) are not written.
  * ---------------------------------------------------------------------- */
 typedef struct {
@@ -248,6 +248,61 @@ typedef struct {
 } lkv_expand_args;
 
 lkv_status lkv_gqla_expand_latent(const lkv_expand_args *args);
+
+/* ------------------------------------------------------------------------
+ * lkv_absorb_query / lkv_up_project -- the per-head projections on either
+ * side of absorbed decode [GQLA section 2, MQA-absorbed path: W_UK folds
+ * into the query, W_UV into the output].  For query row (b, t, h), with
+ * weight block wb = h / (h_q / n_w) of w [n_w, d_c, d_h] (n_w = h_q for
+ * per-head weights, n_w = g for GQLA's group-indexed weights):
+ *   lkv_absorb_query   y[b,t,h,k] = sum_d w[wb][k][d] * x[b,t,h,d]
+ *                      (x: the per-head query [batch, s_q, h_q, d_h];
+ *                       y: the absorbed query [batch, s_q, h_q, d_c])
+ *   lkv_up_project     y[b,t,h,d] = sum_k x[b,t,h,k] * w[wb][k][d]
+ *                      (x: the latent output [batch, s_q, h_q, d_c];
+ *                       y: [batch, s_q, h_q, d_h])
+ * float32 accumulation, bf16 output (round to nearest even).
+ *   x, w, y  device bf16, dense row-major as shown, 16-byte aligned
+ * Supported: bf16, d_c and d_h multiples of 64; h_q a multiple of n_w.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  uint32_t struct_size;
+  int32_t dtype;
+  int32_t batch, s_q, h_q, n_w, d_c, d_h;
+  const void *x;
+  const void *w;
+  void *y;
+  void *stream;
+} lkv_proj_args;
+
+lkv_status lkv_absorb_query(const lkv_proj_args *args);
+lkv_status lkv_up_project(const lkv_proj_args *args);
+
+/* ------------------------------------------------------------------------
+ * lkv_append_tokens -- cache write of a step's new tokens [GQLA section 2:
+ * every token's latent (plus the shared RoPE key) is cached once].  Row t of
+ * sequence b's new rows is copied to logical position j = seqlens[b] - s_q
+ * + t (skipped when j < 0), i.e. cache row
+ * block_table[b][j / page_size]*page_size + j % page_size.
+ *   src      device [batch, s_q, width] elements (dtype), dense
+ *   cache    device, row r at r*tok_stride elements
+ *   seqlens  device int32 [batch]: lengths including the new tokens
+ * Supported: bf16 or f32; width*element size and tok_stride*element size
+ * multiples of 16 bytes; src and cache 16-byte aligned; tok_stride >= width.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  uint32_t struct_size;
+  int32_t dtype;
+  int32_t batch, s_q, width, page_size, max_pages;
+  const void *src;
+  void *cache;
+  int64_t tok_stride;
+  const int32_t *block_table;
+  const int32_t *seqlens;
+  void *stream;
+} lkv_append_args;
+
+lkv_status lkv_append_tokens(const lkv_append_args *args);
 
 /* ------------------------------------------------------------------------
  * lkv_split_combine -- merge split-KV partial results with their LSEs.

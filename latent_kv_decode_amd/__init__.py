@@ -12,6 +12,9 @@ Entry points (same names as the C ABI):
   lkv_gqa_decode          grouped-query decode over an expanded cache (GQLA GQA path, plain GQA)
   lkv_gqla_expand_latent  latent -> g key/value groups at cache-write time
   lkv_split_combine       LSE-weighted merge of split-KV partial results
+  lkv_absorb_query        W_UK folded into the per-head query (before decode)
+  lkv_up_project          W_UV applied to the latent output (after decode)
+  lkv_append_tokens       cache write of a step's new tokens
 plus lkv_mla_decode_workspace_size / lkv_gqa_decode_workspace_size,
 lkv_abi_version and lkv_last_error.
 """
@@ -30,7 +33,7 @@ STATUS_NAMES = {0: "LKV_OK", 1: "LKV_ERR_NULL", 2: "LKV_ERR_SHAPE", 3: "LKV_ERR_
 
 EXPORTED = ["lkv_abi_version", "lkv_last_error", "lkv_mla_decode", "lkv_mla_decode_workspace_size",
             "lkv_gqa_decode", "lkv_gqa_decode_workspace_size", "lkv_gqla_expand_latent",
-            "lkv_split_combine"]
+            "lkv_split_combine", "lkv_absorb_query", "lkv_up_project", "lkv_append_tokens"]
 
 _V = ctypes.c_void_p
 _I = ctypes.c_int32
@@ -73,6 +76,18 @@ class CombineArgs(ctypes.Structure):
                 ("work_offsets", _V), ("out", _V), ("lse", _V), ("stream", _V)]
 
 
+class ProjArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("dtype", _I), ("batch", _I), ("s_q", _I),
+                ("h_q", _I), ("n_w", _I), ("d_c", _I), ("d_h", _I), ("x", _V), ("w", _V),
+                ("y", _V), ("stream", _V)]
+
+
+class AppendArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("dtype", _I), ("batch", _I), ("s_q", _I),
+                ("width", _I), ("page_size", _I), ("max_pages", _I), ("src", _V), ("cache", _V),
+                ("tok_stride", _L), ("block_table", _V), ("seqlens", _V), ("stream", _V)]
+
+
 class LkvError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -94,7 +109,9 @@ def load_library(path: str = LIB_PATH):
         lib.lkv_last_error.restype = ctypes.c_char_p
         for name, argt in [("lkv_mla_decode", MlaArgs), ("lkv_gqa_decode", GqaArgs),
                            ("lkv_gqla_expand_latent", ExpandArgs),
-                           ("lkv_split_combine", CombineArgs)]:
+                           ("lkv_split_combine", CombineArgs),
+                           ("lkv_absorb_query", ProjArgs), ("lkv_up_project", ProjArgs),
+                           ("lkv_append_tokens", AppendArgs)]:
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
             fn.argtypes = [ctypes.POINTER(argt)]
@@ -358,3 +375,50 @@ def lkv_split_combine(o_part, lse_part, work_offsets, *, out=None, lse=None, dty
     a.stream = _stream(stream)
     _check(load_library().lkv_split_combine(ctypes.byref(a)))
     return out, lse
+
+
+def _proj(name, x, w, out, stream, up):
+    torch = _torch()
+    B, s_q, h_q, k = x.shape
+    n_w, d_c, d_h = w.shape
+    if out is None:
+        out = torch.empty((B, s_q, h_q, d_h if up else d_c), dtype=x.dtype, device=x.device)
+    a = ProjArgs()
+    a.struct_size = ctypes.sizeof(ProjArgs)
+    a.dtype = _dtype_code(x)
+    a.batch, a.s_q, a.h_q, a.n_w, a.d_c, a.d_h = B, s_q, h_q, n_w, d_c, d_h
+    a.x, a.w, a.y = _ptr(x), _ptr(w), _ptr(out)
+    a.stream = _stream(stream)
+    _check(getattr(load_library(), name)(ctypes.byref(a)))
+    return out
+
+
+def lkv_absorb_query(q, w_uk, *, out=None, stream=None):
+    """W_UK folded into the query (lkv.h: lkv_absorb_query): q [B, s_q, h_q,
+    d_h], w_uk [n_w, d_c, d_h] -> [B, s_q, h_q, d_c]."""
+    return _proj("lkv_absorb_query", q, w_uk, out, stream, up=False)
+
+
+def lkv_up_project(o_latent, w_uv, *, out=None, stream=None):
+    """W_UV applied to the latent output (lkv.h: lkv_up_project): o_latent
+    [B, s_q, h_q, d_c], w_uv [n_w, d_c, d_h] -> [B, s_q, h_q, d_h]."""
+    return _proj("lkv_up_project", o_latent, w_uv, out, stream, up=True)
+
+
+def lkv_append_tokens(src, cache, block_table, seqlens, *, page_size, tok_stride=None,
+                      stream=None):
+    """Cache write of a step's new tokens (lkv.h: lkv_append_tokens): src
+    [B, s_q, width] rows go to positions seqlens[b] - s_q + t of the paged
+    cache (base pointer; row r at r * tok_stride elements)."""
+    B, s_q, width = src.shape
+    a = AppendArgs()
+    a.struct_size = ctypes.sizeof(AppendArgs)
+    a.dtype = _dtype_code(src)
+    a.batch, a.s_q, a.width = B, s_q, width
+    a.page_size, a.max_pages = page_size, block_table.shape[1]
+    a.src, a.cache = _ptr(src), _ptr(cache)
+    a.tok_stride = width if tok_stride is None else tok_stride
+    a.block_table, a.seqlens = _ptr(block_table), _ptr(seqlens)
+    a.stream = _stream(stream)
+    _check(load_library().lkv_append_tokens(ctypes.byref(a)))
+    return cache

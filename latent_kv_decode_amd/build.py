@@ -22,7 +22,8 @@ BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "decode_mfma.hip", "decode_split.hip", "decode_f32.hip", "combine.hip", "expand.hip"]
+SOURCES = ["abi.cpp", "decode_mfma.hip", "decode_split.hip", "decode_f32.hip", "combine.hip", "expand.hip",
+           "proj.hip"]
 
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

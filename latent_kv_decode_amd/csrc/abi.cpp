@@ -375,6 +375,69 @@ lkv_status lkv_gqla_expand_latent(const lkv_expand_args *a) {
   return LKV_OK;
 }
 
+static lkv_status run_proj(const lkv_proj_args *a, bool up) {
+  if (!a) return fail(LKV_ERR_NULL, "args is NULL");
+  if (a->struct_size != sizeof(lkv_proj_args)) return fail(LKV_ERR_STRUCT, "struct_size %u != %zu", a->struct_size, sizeof(lkv_proj_args));
+  if (a->dtype != LKV_BF16) return fail(LKV_ERR_UNSUPPORTED, "projections are bf16 only");
+  if (a->batch < 0 || a->s_q < 1 || a->h_q < 1 || a->n_w < 1 || a->h_q % a->n_w)
+    return fail(LKV_ERR_SHAPE, "h_q %d must be a positive multiple of n_w %d (batch %d, s_q %d)", a->h_q, a->n_w, a->batch, a->s_q);
+  if (!lkv::proj_supported(a->d_c, a->d_h))
+    return fail(LKV_ERR_UNSUPPORTED, "projections need d_c and d_h multiples of 64; got %d, %d", a->d_c, a->d_h);
+  if (!a->x || !a->w || !a->y) return fail(LKV_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(a->x) || !aligned16(a->w) || !aligned16(a->y)) return fail(LKV_ERR_ALIGN, "x, w and y must be 16-byte aligned");
+  if ((long long)a->batch * a->s_q * a->h_q > (1LL << 30)) return fail(LKV_ERR_SHAPE, "batch * s_q * h_q exceeds 2^30 rows");
+  if (a->batch == 0) return LKV_OK;
+  lkv::ProjParams p{};
+  p.x = a->x;
+  p.w = a->w;
+  p.y = a->y;
+  p.B = a->batch;
+  p.s_q = a->s_q;
+  p.h_q = a->h_q;
+  p.n_w = a->n_w;
+  p.d_c = a->d_c;
+  p.d_h = a->d_h;
+  hipError_t e = lkv::launch_proj(p, up, static_cast<hipStream_t>(a->stream));
+  if (e == hipErrorInvalidValue) return fail(LKV_ERR_SHAPE, "too many tiles for one launch");
+  if (e != hipSuccess) return hip_fail(e, up ? "up-projection launch" : "absorb launch");
+  return LKV_OK;
+}
+
+lkv_status lkv_absorb_query(const lkv_proj_args *a) { return run_proj(a, false); }
+
+lkv_status lkv_up_project(const lkv_proj_args *a) { return run_proj(a, true); }
+
+lkv_status lkv_append_tokens(const lkv_append_args *a) {
+  if (!a) return fail(LKV_ERR_NULL, "args is NULL");
+  if (a->struct_size != sizeof(lkv_append_args)) return fail(LKV_ERR_STRUCT, "struct_size %u != %zu", a->struct_size, sizeof(lkv_append_args));
+  if (a->dtype != LKV_F32 && a->dtype != LKV_BF16) return fail(LKV_ERR_UNSUPPORTED, "dtype %d", a->dtype);
+  if (a->batch < 0 || a->s_q < 1 || a->width < 1 || a->page_size < 1 || a->max_pages < 1)
+    return fail(LKV_ERR_SHAPE, "non-positive size");
+  if ((long long)a->page_size * a->max_pages > (1LL << 30)) return fail(LKV_ERR_SHAPE, "page_size * max_pages exceeds 2^30 tokens");
+  const int es = a->dtype == LKV_BF16 ? 2 : 4;
+  if (a->tok_stride < a->width) return fail(LKV_ERR_SHAPE, "tok_stride %lld < width %d", (long long)a->tok_stride, a->width);
+  if (((long long)a->width * es) % 16 || (a->tok_stride * es) % 16)
+    return fail(LKV_ERR_ALIGN, "width and tok_stride must be multiples of 16 bytes");
+  if (!a->src || !a->cache || !a->block_table || !a->seqlens) return fail(LKV_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(a->src) || !aligned16(a->cache)) return fail(LKV_ERR_ALIGN, "src and cache must be 16-byte aligned");
+  if ((long long)a->batch * a->s_q > (1LL << 30)) return fail(LKV_ERR_SHAPE, "batch * s_q exceeds 2^30 rows");
+  if (a->batch == 0) return LKV_OK;
+  lkv::AppendParams p{};
+  p.src = a->src;
+  p.cache = a->cache;
+  p.block_table = a->block_table;
+  p.seqlens = a->seqlens;
+  p.B = a->batch;
+  p.s_q = a->s_q;
+  p.page_size = a->page_size;
+  p.max_pages = a->max_pages;
+  p.row_bytes = a->width * es;
+  p.tok_stride_bytes = a->tok_stride * es;
+  hipError_t e = lkv::launch_append(p, static_cast<hipStream_t>(a->stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return LKV_OK;
+}
+
 lkv_status lkv_split_combine(const lkv_combine_args *a) {
   if (!a) return fail(LKV_ERR_NULL, "args is NULL");
   if (a->struct_size != sizeof(lkv_combine_args)) return fail(LKV_ERR_STRUCT, "struct_size %u != %zu", a->struct_size, sizeof(lkv_combine_args));

@@ -68,6 +68,22 @@ struct CombineParams {
   int out_bf16;
 };
 
+struct ProjParams {
+  const void *x;                // [B, s_q, h_q, K] rows
+  const void *w;                // [n_w, d_c, d_h]
+  void *y;                      // [B, s_q, h_q, N] rows
+  int B, s_q, h_q, n_w, d_c, d_h;
+};
+
+struct AppendParams {
+  const void *src;              // [B, s_q] rows of row_bytes
+  void *cache;                  // cache row r at r * tok_stride_bytes
+  const int32_t *block_table, *seqlens;
+  int B, s_q, page_size, max_pages;
+  int row_bytes;
+  long long tok_stride_bytes;
+};
+
 struct ExpandParams {
   const void *c;                // latent, row r at r*c_stride
   long long c_stride;
@@ -95,6 +111,10 @@ int mla_split_rows();
 hipError_t launch_mla_split(const DecodeParams &p, hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_f32_decode(const DecodeParams &p, hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_combine(const CombineParams &p, hipStream_t s);
+bool proj_supported(int d_c, int d_h);
+// up == false: q' = W_UK q (d_h -> d_c); up == true: o = O' W_UV (d_c -> d_h)
+hipError_t launch_proj(const ProjParams &p, bool up, hipStream_t s);
+hipError_t launch_append(const AppendParams &p, hipStream_t s);
 bool expand_supported(int d_c, int d_h);
 hipError_t launch_expand(const ExpandParams &p, hipStream_t s);
 

@@ -316,3 +316,23 @@ def lse_combine(o_part, lse_part, work_offsets):
     lse = np.empty((B, s_q, h_q))
     _load().oracle_lse_combine(B, s_q, h_q, d_v, _ptr(o), _ptr(l), _ptr(off), _ptr(out), _ptr(lse))
     return out, lse
+
+
+def append_tokens(src, cache, block_table, seqlens, *, page_size, tok_stride):
+    """Cache write of a step's new tokens (GQLA section 2: every token's latent
+    and the shared RoPE key are cached once, per page slot).  Row t of
+    sequence b's s_q new rows goes to logical position j = seqlens[b] - s_q +
+    t (skipped when j < 0), physical row block_table[b][j // page_size] *
+    page_size + j % page_size.  Pure data movement, written out here with
+    plain loops.  Returns a flat copy of ``cache`` with those rows written."""
+    out = np.array(cache, copy=True).reshape(-1)
+    src = np.asarray(src)
+    B, s_q, width = src.shape
+    for b in range(B):
+        for t in range(s_q):
+            j = int(seqlens[b]) - s_q + t
+            if j < 0:
+                continue
+            row = int(block_table[b, j // page_size]) * page_size + j % page_size
+            out[row * tok_stride: row * tok_stride + width] = src[b, t]
+    return out

@@ -53,7 +53,9 @@ def _c_layout(struct, fields):
 
 @pytest.mark.parametrize("py,c", [(lkv.MlaArgs, "lkv_mla_args"), (lkv.GqaArgs, "lkv_gqa_args"),
                                   (lkv.ExpandArgs, "lkv_expand_args"),
-                                  (lkv.CombineArgs, "lkv_combine_args")])
+                                  (lkv.CombineArgs, "lkv_combine_args"),
+                                  (lkv.ProjArgs, "lkv_proj_args"),
+                                  (lkv.AppendArgs, "lkv_append_args")])
 def test_struct_layouts_match_header(py, c):
     fields = [f for f, _ in py._fields_]
     size, offs = _c_layout(c, fields)
@@ -192,6 +194,54 @@ def _combine(**kw):
 def test_combine_validation(lib, change, expect):
     st = lib.lkv_split_combine(ctypes.byref(_combine(**change)))
     assert st == expect, (st, lkv.lkv_last_error())
+
+
+def _proj(**kw):
+    a = lkv.ProjArgs()
+    a.struct_size = ctypes.sizeof(lkv.ProjArgs)
+    a.dtype = lkv.LKV_BF16
+    a.batch, a.s_q, a.h_q, a.n_w, a.d_c, a.d_h = 2, 1, 128, 8, 512, 128
+    a.x = a.w = a.y = FAKE
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("fn", ["lkv_absorb_query", "lkv_up_project"])
+@pytest.mark.parametrize("change,expect", [
+    (dict(struct_size=8), 7), (dict(dtype=0), 3), (dict(h_q=100), 2), (dict(n_w=0), 2),
+    (dict(d_c=96), 3), (dict(d_h=32), 3), (dict(x=None), 1), (dict(y=FAKE + 8), 4),
+    (dict(s_q=0), 2)])
+def test_proj_validation(lib, fn, change, expect):
+    st = getattr(lib, fn)(ctypes.byref(_proj(**change)))
+    assert st == expect, (st, lkv.lkv_last_error())
+
+
+def _append(**kw):
+    a = lkv.AppendArgs()
+    a.struct_size = ctypes.sizeof(lkv.AppendArgs)
+    a.dtype = lkv.LKV_BF16
+    a.batch, a.s_q, a.width, a.page_size, a.max_pages = 2, 1, 576, 64, 4
+    a.src = a.cache = a.block_table = a.seqlens = FAKE
+    a.tok_stride = 576
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(struct_size=8), 7), (dict(dtype=4), 3), (dict(width=0), 2), (dict(width=580, tok_stride=1168), 4),
+    (dict(tok_stride=500), 2), (dict(tok_stride=580), 4), (dict(cache=FAKE + 2), 4),
+    (dict(seqlens=None), 1), (dict(page_size=0), 2)])
+def test_append_validation(lib, change, expect):
+    st = lib.lkv_append_tokens(ctypes.byref(_append(**change)))
+    assert st == expect, (st, lkv.lkv_last_error())
+
+
+def test_proj_and_append_batch_zero_ok(lib):
+    assert lib.lkv_absorb_query(ctypes.byref(_proj(batch=0, x=None, w=None, y=None))) == 1
+    assert lib.lkv_absorb_query(ctypes.byref(_proj(batch=0))) == 0
+    assert lib.lkv_append_tokens(ctypes.byref(_append(batch=0))) == 0
 
 
 def test_binding_raises_when_library_missing(tmp_path):

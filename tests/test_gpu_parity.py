@@ -402,6 +402,83 @@ def test_gqla_grouped_and_absorbed_paths(lkv, oracle):
     assert_close(o_abs, ro, from_dev(lse_a), rl, what="gqla absorbed (GPU) + W_UV vs oracle grouped")
 
 
+# ------------------------------------------- steps either side of decode
+@pytest.mark.parametrize("B,s_q,h_q,n_w,d_c,d_h", [
+    (3, 2, 16, 16, 512, 128),    # per-head weights (MLA)
+    (2, 2, 128, 8, 512, 128),    # group-indexed weights (GQLA)
+    (5, 1, 12, 3, 256, 64)])     # row count not a multiple of the 64-row tile
+def test_absorb_and_up_project_match_oracle(lkv, oracle, B, s_q, h_q, n_w, d_c, d_h):
+    rng = np.random.default_rng(900 + h_q + d_c)
+    q = li.to_bf16_bits(rng.standard_normal((B, s_q, h_q, d_h)).astype(np.float32))
+    o = li.to_bf16_bits(rng.standard_normal((B, s_q, h_q, d_c)).astype(np.float32))
+    w = li.to_bf16_bits((rng.standard_normal((n_w, d_c, d_h)) / math.sqrt(d_c)).astype(np.float32))
+    note(f"case projections B={B} s_q={s_q} h_q={h_q} n_w={n_w} d_c={d_c} d_h={d_h}")
+    f = lambda a: li.bf16_bits_to_f32(a).astype(np.float64)
+    for name, x, ref_fn in (("absorb", q, oracle.absorb_query), ("up", o, oracle.up_project)):
+        fn = lkv.lkv_absorb_query if name == "absorb" else lkv.lkv_up_project
+        got = from_dev(fn(to_dev(x, torch), to_dev(w, torch)))
+        ref = ref_fn(f(x), f(w))
+        mag = ref_fn(np.abs(f(x)), np.abs(f(w)))  # sum of |terms| per output
+        # one bf16 rounding of the output plus float32 accumulation
+        tol = 2.0 ** -8 * np.abs(ref) + 2.0 ** -18 * mag + 1e-30
+        err = np.abs(got - ref)
+        note(f"  {name}: max err/tol {float((err / tol).max()):.3f}")
+        assert (err <= tol).all(), name
+
+
+def test_append_tokens_bit_exact(lkv, oracle):
+    w, x = small_mla(910, B=3, s_q=2, seqlens=[130, 2, 64])
+    width = w.n_lat * w.d_c + w.d_rope
+    rng = np.random.default_rng(911)
+    src = li.to_bf16_bits(rng.standard_normal((w.B, w.s_q, width)).astype(np.float32))
+    kv = to_dev(x["kv"], torch)
+    note("case append")
+    lkv.lkv_append_tokens(to_dev(src, torch), kv, torch.from_numpy(x["block_table"]).cuda(),
+                          torch.from_numpy(x["seqlens"]).cuda(), page_size=w.page_size)
+    torch.cuda.synchronize()
+    got = kv.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1)
+    ref = oracle.append_tokens(src, x["kv"], x["block_table"], x["seqlens"],
+                               page_size=w.page_size, tok_stride=width)
+    assert np.array_equal(got.view(np.uint16), ref.view(np.uint16).reshape(-1))
+
+
+def test_decode_layer_on_gpu(lkv, oracle):
+    """The whole absorbed decode layer on the GPU -- W_UK into the query,
+    the step's new tokens into the cache, latent decode, W_UV on the output
+    -- against the oracle's grouped path on the same weights."""
+    w, x = _gqla_small(920)
+    width = w.d_c + w.d_rope
+    P = w.page_size
+    # the cache as it stood before this step: the last s_q tokens of each
+    # sequence are absent (NaN) and come in through the append
+    kv0 = x["kv"].copy()
+    for b, L in enumerate(x["seqlens"]):
+        for j in range(int(L) - w.s_q, int(L)):
+            kv0[x["block_table"][b, j // P], j % P] = li.BF16_NAN
+    new = np.stack([np.stack([x["kv"][x["block_table"][b, j // P], j % P]
+                              for j in range(int(L) - w.s_q, int(L))])
+                    for b, L in enumerate(x["seqlens"])])
+    kv = to_dev(kv0, torch)
+    flat = kv.reshape(-1)
+    bt, sl = torch.from_numpy(x["block_table"]).cuda(), torch.from_numpy(x["seqlens"]).cuda()
+    note("case decode layer")
+    lkv.lkv_append_tokens(to_dev(new, torch), kv, bt, sl, page_size=P)
+    q_abs = lkv.lkv_absorb_query(to_dev(x["q_nope_h"], torch), to_dev(x["w_uk"], torch))
+    out, lse = lkv.lkv_mla_decode(q_abs, to_dev(x["q_rope"], torch), flat, flat[w.d_c:], bt, sl,
+                                  page_size=P, softmax_scale=w.scale, kv_tok_stride=width,
+                                  rope_tok_stride=width, seqlens_host=x["seqlens"])
+    o = lkv.lkv_up_project(out, to_dev(x["w_uv"], torch))
+    wuk, wuv = _w64(x, "w_uk"), _w64(x, "w_uv")
+    rk, rv = oracle.expand_latent(x["kv"].reshape(-1), wuk, wuv, x["block_table"], x["seqlens"],
+                                  page_size=P, num_pages=x["num_pages"], kv_tok_stride=width)
+    kv64 = li.bf16_bits_to_f32(x["kv"]).astype(np.float64)
+    ro, rl = oracle.gqa_decode(_w64(x, "q_nope_h"), np.nan_to_num(rk), np.nan_to_num(rv),
+                               x["block_table"], x["seqlens"], n_kv=w.n_kv, d_h=w.d_h,
+                               page_size=P, scale=w.scale, q_rope=_w64(x, "q_rope"),
+                               k_rope=np.nan_to_num(kv64[..., w.d_c:]).copy(), d_rope=w.d_rope)
+    assert_close(from_dev(o), ro, from_dev(lse), rl, what="decode layer (GPU) vs oracle grouped")
+
+
 # ------------------------------------------------------------ split combine
 def test_split_combine_entry_point(lkv, oracle):
     rng = np.random.default_rng(800)

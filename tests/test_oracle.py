@@ -408,3 +408,38 @@ def test_tiny_fp32_workload_runs_fast(oracle_lib):
     assert time.perf_counter() - t0 < 1.0
     assert np.isfinite(o).all() and np.isfinite(l).all()
     assert x["num_pages"] == 29
+
+
+def test_append_tokens_rebuilds_the_generated_cache(oracle_lib):
+    """Appending every valid token of a generated batch, a few tokens per
+    step from an empty cache, reproduces the paged layout that lkv_inputs
+    builds on its own (its valid slots bit for bit; the other slots stay
+    untouched)."""
+    w = li.Workload(name="app", kind="mla", dtype="bf16", B=3, h_q=16, s_q=1, page_size=16,
+                    n_lat=1, d_c=64, d_rope=16, seqlens=(37, 16, 5), table="fragmented",
+                    scale=0.1, seed=31)
+    x = li.generate(w)
+    kv = x["kv"]  # [num_pages, page_size, width], unused slots NaN
+    npg, P, width = kv.shape
+    bt, sl = x["block_table"], x["seqlens"]
+    # the logical rows of each sequence, read through the table
+    logical = [np.stack([kv[bt[b, j // P], j % P] for j in range(int(sl[b]))]) for b in range(w.B)]
+    sentinel = np.uint16(0x1234)
+    cache = np.full(npg * P * width, sentinel, np.uint16)
+    step = 3
+    for L_done in range(0, int(sl.max()), step):
+        s_q = step
+        lens = np.minimum(sl, L_done + s_q).astype(np.int32)
+        src = np.full((w.B, s_q, width), sentinel, np.uint16)
+        for b in range(w.B):
+            for t in range(s_q):
+                j = int(lens[b]) - s_q + t
+                if j >= L_done:  # a new token of this step
+                    src[b, t] = logical[b][j]
+                elif j >= 0:     # already written: write the same row again
+                    src[b, t] = logical[b][j]
+        cache = oracle_lib.append_tokens(src, cache, bt, lens, page_size=P, tok_stride=width)
+    got = cache.reshape(npg, P, width)
+    valid = li.valid_slot_mask(bt, sl, P, npg)
+    assert np.array_equal(got[valid], kv[valid])
+    assert (got[~valid] == sentinel).all()
