@@ -14,6 +14,8 @@ the split-KV combine).  Other workloads (lkv_inputs.WORKLOADS):
   gqla_grouped_b64_l4096_sq2   GQLA grouped path: the latent is expanded into
                                8 key/value groups once (timed separately, not
                                part of the step), then grouped decode
+  dsv3_mla_b64_l4096_fp8, gla2_b128_l8192_fp8, gqa_b128_l8192_fp8
+                               the same with 8-bit (OCP E4M3) caches
 
 Timing: W untimed warm-up steps (default 150: the first ~100 steps of a run
 are up to 20% slower while the chip settles), then K timed steps bracketed by
@@ -141,6 +143,23 @@ def timed_oracle(run_seqs, B: int, budget_s: float):
     return done, elapsed
 
 
+def oracle_inputs(x, w, keys, qkeys):
+    """The oracle's copies of the inputs: an 8-bit cache dequantised to
+    float32 (exact: E4M3 values times a power-of-two scale) through the
+    oracle's own E4M3 decoding of all 256 codes, the queries widened to match;
+    other workloads pass through.  Computed once."""
+    if w.cache != "fp8":
+        return x
+    if "_oracle_copy" not in x:
+        import oracle
+        import lkv_inputs as li
+        lut = oracle.e4m3_to_f64(np.arange(256, dtype=np.uint8), x["kv_scale"]).astype(np.float32)
+        y = {k: lut[x[k]] for k in keys}
+        y.update({k: li.bf16_bits_to_f32(x[k]) for k in qkeys})
+        x["_oracle_copy"] = y
+    return {**x, **x["_oracle_copy"]}
+
+
 def rel_l2(got, ref):
     return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
 
@@ -159,6 +178,8 @@ def setup_mla(w, x, args, torch, lkv, rf):
     out = torch.empty((w.B, w.s_q, w.h_q, w.d_c), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.B, w.s_q, w.h_q), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+    fp8 = w.cache == "fp8"
+    q8 = dict(kv_fp8=True, kv_scale=w.kv_scale) if fp8 else {}
 
     def step(i, events=None):
         kv = kvs[i % ROTATE]
@@ -166,11 +187,12 @@ def setup_mla(w, x, args, torch, lkv, rf):
                            page_size=w.page_size, softmax_scale=w.scale, causal=w.causal,
                            kv_tok_stride=width, rope_tok_stride=width, num_splits=args.num_splits,
                            seqlens_host=x["seqlens"], out=out, lse=lse, stream=stream,
-                           kernel_events=events)
+                           kernel_events=events, **q8)
 
     def oracle_rows(rows):
-        kv0 = x["kv"].reshape(-1)
-        return oracle.mla_decode(x["q_nope"], x["q_rope"], kv0, kv0[w.n_lat * w.d_c:],
+        y = oracle_inputs(x, w, ["kv"], ["q_nope", "q_rope"])
+        kv0 = y["kv"].reshape(-1)
+        return oracle.mla_decode(y["q_nope"], y["q_rope"], kv0, kv0[w.n_lat * w.d_c:],
                                  x["block_table"], x["seqlens"], n_lat=w.n_lat, d_c=w.d_c,
                                  d_rope=w.d_rope, page_size=w.page_size, scale=w.scale,
                                  causal=w.causal, kv_tok_stride=width, rope_tok_stride=width,
@@ -191,11 +213,14 @@ def setup_mla(w, x, args, torch, lkv, rf):
                          f"each, full cache length) of the timed workload"
 
     work = rf.mla_work(x["seqlens"], s_q=w.s_q, h_q=w.h_q, n_lat=w.n_lat, d_c=w.d_c,
-                       d_rope=w.d_rope, page_size=w.page_size, causal=w.causal)
-    many_rows = w.h_q // w.n_lat * w.s_q > 32 and w.d_c in (256, 512)
+                       d_rope=w.d_rope, page_size=w.page_size, causal=w.causal,
+                       cache_elem=1 if fp8 else 2)
+    # the many-row split kernel reads bf16 caches only
+    many_rows = w.h_q // w.n_lat * w.s_q > 32 and w.d_c in (256, 512) and not fp8
     return dict(step=step, work=work, parity=parity, cpu=cpu,
                 kernel="mla_split_kernel" if many_rows else "mfma_decode_kernel",
-                config={"n_latent": w.n_lat, "d_c": w.d_c, "d_rope": w.d_rope})
+                config={"n_latent": w.n_lat, "d_c": w.d_c, "d_rope": w.d_rope,
+                        "cache": "e4m3" if fp8 else "bf16"})
 
 
 def setup_gqa(w, x, args, torch, lkv, rf):
@@ -212,15 +237,18 @@ def setup_gqa(w, x, args, torch, lkv, rf):
     out = torch.empty((w.B, w.s_q, w.h_q, w.d_h), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.B, w.s_q, w.h_q), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+    fp8 = w.cache == "fp8"
+    q8 = dict(kv_fp8=True, kv_scale=w.kv_scale) if fp8 else {}
 
     def step(i, events=None):
         lkv.lkv_gqa_decode(q, None, ks[i % ROTATE], vs[i % ROTATE], None, bt, sl, n_kv=w.n_kv,
                            page_size=w.page_size, softmax_scale=w.scale, causal=w.causal,
                            num_splits=args.num_splits, seqlens_host=x["seqlens"], out=out,
-                           lse=lse, stream=stream, kernel_events=events)
+                           lse=lse, stream=stream, kernel_events=events, **q8)
 
     def oracle_rows(rows):
-        return oracle.gqa_decode(x["q"], x["k_cache"], x["v_cache"], x["block_table"],
+        y = oracle_inputs(x, w, ["k_cache", "v_cache"], ["q"])
+        return oracle.gqa_decode(y["q"], y["k_cache"], y["v_cache"], x["block_table"],
                                  x["seqlens"], n_kv=w.n_kv, d_h=w.d_h, page_size=w.page_size,
                                  scale=w.scale, causal=w.causal, rows=rows)
 
@@ -238,9 +266,10 @@ def setup_gqa(w, x, args, torch, lkv, rf):
         return done, el, f"{done} of {w.B} sequences (all {w.h_q} heads) of the timed workload"
 
     work = rf.gqa_work(x["seqlens"], s_q=w.s_q, h_q=w.h_q, n_kv=w.n_kv, d_h=w.d_h, d_rope=0,
-                       page_size=w.page_size, causal=w.causal)
+                       page_size=w.page_size, causal=w.causal, cache_elem=1 if fp8 else 2)
     return dict(step=step, work=work, parity=parity, cpu=cpu, kernel="mfma_decode_kernel",
-                config={"n_kv": w.n_kv, "d_h": w.d_h, "d_rope": 0})
+                config={"n_kv": w.n_kv, "d_h": w.d_h, "d_rope": 0,
+                        "cache": "e4m3" if fp8 else "bf16"})
 
 
 def setup_gqla(w, x, args, torch, lkv, rf):

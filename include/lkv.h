@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define LKV_ABI_VERSION 1
+#define LKV_ABI_VERSION 2
 
 typedef enum {
   LKV_OK = 0,
@@ -120,6 +120,17 @@ const char *lkv_last_error(void);
  *   seqlens_host  host int32 [batch] copy of seqlens, or NULL.  Used only to
  *           skip the combine pass when no sequence is split; it must then
  *           equal the device values.
+ *   kv_fp8, kv_scale  8-bit cache: with kv_fp8 nonzero, c_kv and k_rope hold
+ *           OCP 8-bit float E4M3 codes x8 (one byte per element, strides in
+ *           bytes) of the values kv_scale * x8, one scale for every cache of
+ *           the call; queries and output stay bf16.  Each code converts
+ *           exactly to bf16, so the arithmetic is that of the bf16 path on
+ *           the dequantised values.  Needs dtype LKV_BF16, kv_scale positive
+ *           and finite, cache strides multiples of 16 and the widths
+ *           (d_c, d_rope) in {(512, 64), (256, 64), (128, 64)}; every row
+ *           count (more than 32 rows per latent head run as 32-row tiles
+ *           that read the cache through L2).  kv_fp8 = 0: the caches hold
+ *           the dtype of the inputs and kv_scale is ignored.
  *   kernel_events  optional pair of hipEvent_t (either may be NULL), for
  *           timing the attention kernel alone (not the combine pass): they
  *           are attached to that kernel's launch (hipExtLaunchKernel) and
@@ -153,6 +164,8 @@ typedef struct {
   size_t workspace_bytes;
   void *stream; /* hipStream_t */
   void *kernel_events[2]; /* hipEvent_t or NULL each */
+  int32_t kv_fp8;  /* nonzero: 8-bit cache, see above */
+  float kv_scale;  /* its dequantisation scale */
 } lkv_mla_args;
 
 lkv_status lkv_mla_decode(const lkv_mla_args *args);
@@ -176,7 +189,9 @@ lkv_status lkv_mla_decode_workspace_size(const lkv_mla_args *args, size_t *bytes
  *   v_cache  device, element (p, s, g, d) at (p*page_size + s)*v_tok_stride + g*d_h + d
  *   k_rope   device, as in lkv_mla_args; NULL iff d_rope == 0
  *   out      device [batch, s_q, h_q, d_h];  lse device float32 [batch, s_q, h_q] or NULL
- *   workspace / num_splits / seqlens_host / kernel_events as in lkv_mla_args.
+ *   workspace / num_splits / seqlens_host / kernel_events / kv_fp8 /
+ *   kv_scale as in lkv_mla_args (8-bit caches: k_cache, v_cache and k_rope
+ *   all hold codes; (d_h, d_rope) in {(128, 64), (128, 0)}).
  * Supported: bf16 with (d_h, d_rope) in {(128, 64), (128, 0), (64, 0),
  *   (256, 0)}; f32 with d_h + d_rope <= 1024.
  * ---------------------------------------------------------------------- */
@@ -204,6 +219,8 @@ typedef struct {
   size_t workspace_bytes;
   void *stream;
   void *kernel_events[2]; /* hipEvent_t or NULL each */
+  int32_t kv_fp8;  /* as in lkv_mla_args */
+  float kv_scale;
 } lkv_gqa_args;
 
 lkv_status lkv_gqa_decode(const lkv_gqa_args *args);

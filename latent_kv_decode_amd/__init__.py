@@ -48,7 +48,8 @@ class MlaArgs(ctypes.Structure):
                 ("kv_tok_stride", _L), ("k_rope", _V), ("rope_tok_stride", _L),
                 ("block_table", _V), ("seqlens", _V), ("seqlens_host", _V), ("out", _V),
                 ("lse", _V), ("workspace", _V), ("workspace_bytes", ctypes.c_size_t),
-                ("stream", _V), ("kernel_events", _V * 2)]
+                ("stream", _V), ("kernel_events", _V * 2), ("kv_fp8", _I),
+                ("kv_scale", ctypes.c_float)]
 
 
 class GqaArgs(ctypes.Structure):
@@ -59,7 +60,8 @@ class GqaArgs(ctypes.Structure):
                 ("k_tok_stride", _L), ("v_cache", _V), ("v_tok_stride", _L), ("k_rope", _V),
                 ("rope_tok_stride", _L), ("block_table", _V), ("seqlens", _V),
                 ("seqlens_host", _V), ("out", _V), ("lse", _V), ("workspace", _V),
-                ("workspace_bytes", ctypes.c_size_t), ("stream", _V), ("kernel_events", _V * 2)]
+                ("workspace_bytes", ctypes.c_size_t), ("stream", _V), ("kernel_events", _V * 2),
+                ("kv_fp8", _I), ("kv_scale", ctypes.c_float)]
 
 
 class ExpandArgs(ctypes.Structure):
@@ -198,7 +200,8 @@ def _set_events(a, kernel_events):
 
 
 def _mla_args(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, n_latent, page_size,
-              softmax_scale, causal, kv_tok_stride, rope_tok_stride, num_splits):
+              softmax_scale, causal, kv_tok_stride, rope_tok_stride, num_splits, kv_fp8=False,
+              kv_scale=1.0):
     B, s_q, h_q, d_c = q_nope.shape
     d_rope = 0 if q_rope is None else q_rope.shape[-1]
     a = MlaArgs()
@@ -215,14 +218,17 @@ def _mla_args(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, n_latent, page
     a.kv_tok_stride = n_latent * d_c if kv_tok_stride is None else kv_tok_stride
     a.rope_tok_stride = d_rope if rope_tok_stride is None else rope_tok_stride
     a.block_table, a.seqlens = _ptr(block_table), _ptr(seqlens)
+    a.kv_fp8, a.kv_scale = int(bool(kv_fp8)), float(kv_scale)
     return a
 
 
 def lkv_mla_decode_workspace_size(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, *,
                                   n_latent=1, page_size, softmax_scale, causal=True,
-                                  kv_tok_stride=None, rope_tok_stride=None, num_splits=0) -> int:
+                                  kv_tok_stride=None, rope_tok_stride=None, num_splits=0,
+                                  kv_fp8=False, kv_scale=1.0) -> int:
     a = _mla_args(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, n_latent, page_size,
-                  softmax_scale, causal, kv_tok_stride, rope_tok_stride, num_splits)
+                  softmax_scale, causal, kv_tok_stride, rope_tok_stride, num_splits, kv_fp8,
+                  kv_scale)
     n = ctypes.c_size_t(0)
     _check(load_library().lkv_mla_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)))
     return int(n.value)
@@ -231,7 +237,8 @@ def lkv_mla_decode_workspace_size(q_nope, q_rope, c_kv, k_rope, block_table, seq
 def lkv_mla_decode(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, *, n_latent=1,
                    page_size, softmax_scale, causal=True, kv_tok_stride=None,
                    rope_tok_stride=None, num_splits=0, seqlens_host=None, out=None, lse=None,
-                   return_lse=True, workspace=None, stream=None, kernel_events=None):
+                   return_lse=True, workspace=None, stream=None, kernel_events=None,
+                   kv_fp8=False, kv_scale=1.0):
     """MLA absorbed decode (lkv.h: lkv_mla_decode).  Returns (out, lse).
 
     q_nope [B, s_q, h_q, d_c], q_rope [B, s_q, h_q, d_rope] (or None with
@@ -239,10 +246,13 @@ def lkv_mla_decode(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, *, n_late
     offsets follow kv_tok_stride / rope_tok_stride); block_table int32
     [B, max_pages]; seqlens int32 [B] on the device.  kernel_events: optional
     pair of raw hipEvent_t handles (ints) recorded around the attention kernel.
+    kv_fp8 / kv_scale: the caches hold OCP E4M3 codes (torch.uint8) of the
+    values kv_scale * code.
     """
     torch = _torch()
     a = _mla_args(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, n_latent, page_size,
-                  softmax_scale, causal, kv_tok_stride, rope_tok_stride, num_splits)
+                  softmax_scale, causal, kv_tok_stride, rope_tok_stride, num_splits, kv_fp8,
+                  kv_scale)
     lib = load_library()
     B, s_q, h_q, d_c = q_nope.shape
     if out is None:
@@ -266,7 +276,8 @@ def lkv_mla_decode(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, *, n_late
 
 
 def _gqa_args(q, q_rope, k_cache, v_cache, k_rope, block_table, seqlens, n_kv, page_size,
-              softmax_scale, causal, k_tok_stride, v_tok_stride, rope_tok_stride, num_splits):
+              softmax_scale, causal, k_tok_stride, v_tok_stride, rope_tok_stride, num_splits,
+              kv_fp8=False, kv_scale=1.0):
     B, s_q, h_q, d_h = q.shape
     d_rope = 0 if q_rope is None else q_rope.shape[-1]
     a = GqaArgs()
@@ -284,14 +295,17 @@ def _gqa_args(q, q_rope, k_cache, v_cache, k_rope, block_table, seqlens, n_kv, p
     a.v_tok_stride = n_kv * d_h if v_tok_stride is None else v_tok_stride
     a.rope_tok_stride = d_rope if rope_tok_stride is None else rope_tok_stride
     a.block_table, a.seqlens = _ptr(block_table), _ptr(seqlens)
+    a.kv_fp8, a.kv_scale = int(bool(kv_fp8)), float(kv_scale)
     return a
 
 
 def lkv_gqa_decode_workspace_size(q, q_rope, k_cache, v_cache, k_rope, block_table, seqlens, *,
                                   n_kv, page_size, softmax_scale, causal=True, k_tok_stride=None,
-                                  v_tok_stride=None, rope_tok_stride=None, num_splits=0) -> int:
+                                  v_tok_stride=None, rope_tok_stride=None, num_splits=0,
+                                  kv_fp8=False, kv_scale=1.0) -> int:
     a = _gqa_args(q, q_rope, k_cache, v_cache, k_rope, block_table, seqlens, n_kv, page_size,
-                  softmax_scale, causal, k_tok_stride, v_tok_stride, rope_tok_stride, num_splits)
+                  softmax_scale, causal, k_tok_stride, v_tok_stride, rope_tok_stride, num_splits,
+                  kv_fp8, kv_scale)
     n = ctypes.c_size_t(0)
     _check(load_library().lkv_gqa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)))
     return int(n.value)
@@ -300,12 +314,15 @@ def lkv_gqa_decode_workspace_size(q, q_rope, k_cache, v_cache, k_rope, block_tab
 def lkv_gqa_decode(q, q_rope, k_cache, v_cache, k_rope, block_table, seqlens, *, n_kv, page_size,
                    softmax_scale, causal=True, k_tok_stride=None, v_tok_stride=None,
                    rope_tok_stride=None, num_splits=0, seqlens_host=None, out=None, lse=None,
-                   return_lse=True, workspace=None, stream=None, kernel_events=None):
+                   return_lse=True, workspace=None, stream=None, kernel_events=None,
+                   kv_fp8=False, kv_scale=1.0):
     """Grouped-query decode over an expanded cache (lkv.h: lkv_gqa_decode).
-    Returns (out [B, s_q, h_q, d_h], lse); kernel_events as in lkv_mla_decode."""
+    Returns (out [B, s_q, h_q, d_h], lse); kernel_events, kv_fp8 and kv_scale
+    as in lkv_mla_decode."""
     torch = _torch()
     a = _gqa_args(q, q_rope, k_cache, v_cache, k_rope, block_table, seqlens, n_kv, page_size,
-                  softmax_scale, causal, k_tok_stride, v_tok_stride, rope_tok_stride, num_splits)
+                  softmax_scale, causal, k_tok_stride, v_tok_stride, rope_tok_stride, num_splits,
+                  kv_fp8, kv_scale)
     lib = load_library()
     B, s_q, h_q, d_h = q.shape
     if out is None:

@@ -68,6 +68,8 @@ int seq_tiles(int L) { return L <= 0 ? 1 : (L + lkv::kTile - 1) / lkv::kTile; }
 struct Shape {
   int dtype, B, s_q, h_q, n_kvh, dk, dr, dv, page_size, max_pages, causal, num_splits;
   bool v_alias;
+  bool fp8;        // the caches hold OCP E4M3 codes
+  float kv_scale;  // their dequantisation scale
 };
 
 // Kernel for many query rows over one latent head (score and value products
@@ -87,7 +89,7 @@ lkv_status make_plan(const Shape &s, Plan *pl) {
   // Many query rows over one latent: one work-group takes 64 of them and
   // reads each cache tile once for all of them.
   pl->latent = kLatentNone;
-  if (s.dtype == LKV_BF16 && s.v_alias && rows_per_kvh > 32 && lkv::mla_split_supported(s.dk, s.dr))
+  if (s.dtype == LKV_BF16 && !s.fp8 && s.v_alias && rows_per_kvh > 32 && lkv::mla_split_supported(s.dk, s.dr))
     pl->latent = kLatentSplit;
   pl->rows = pl->latent == kLatentSplit ? lkv::mla_split_rows() : lkv::mfma_decode_rows(rows_per_kvh);
   pl->row_tiles = (rows_per_kvh + pl->rows - 1) / pl->rows;
@@ -98,7 +100,7 @@ lkv_status make_plan(const Shape &s, Plan *pl) {
   // chip (CUs x work-groups resident per CU)
   int per_cu = 1;
   if (s.dtype == LKV_BF16 && pl->latent == kLatentNone)
-    per_cu = lkv::mfma_decode_blocks_per_cu(s.dk, s.dr, s.dv, s.v_alias, pl->rows);
+    per_cu = lkv::mfma_decode_blocks_per_cu(s.dk, s.dr, s.dv, s.v_alias, pl->rows, s.fp8);
   int chunks = s.num_splits > 0 ? s.num_splits : std::max(1, cus * per_cu / std::max(1, groups));
   chunks = std::min(chunks, 1 << 20);
   pl->n_chunks = chunks;
@@ -136,10 +138,19 @@ lkv_status check_shape(const Shape &s) {
   if ((long long)s.page_size * s.max_pages > (1LL << 30)) return fail(LKV_ERR_SHAPE, "page_size * max_pages exceeds 2^30 tokens");
   if ((long long)s.B * s.s_q * s.h_q > (1LL << 30)) return fail(LKV_ERR_SHAPE, "batch * s_q * h_q exceeds 2^30 rows");
   if (s.num_splits < 0) return fail(LKV_ERR_SHAPE, "num_splits %d is negative", s.num_splits);
-  if (s.dtype == LKV_BF16) {
+  if (s.fp8) {
+    if (s.dtype != LKV_BF16) return fail(LKV_ERR_UNSUPPORTED, "an 8-bit cache needs bf16 queries and output");
+    if (!(s.kv_scale > 0.f) || !std::isfinite(s.kv_scale))
+      return fail(LKV_ERR_SHAPE, "kv_scale %g must be positive and finite", (double)s.kv_scale);
+    if (!lkv::mfma_decode_supported(s.dk, s.dr, s.dv, s.v_alias, true))
+      return fail(LKV_ERR_UNSUPPORTED,
+                  "no 8-bit-cache kernel for key width %d + RoPE %d, value width %d (%s); compiled: latent "
+                  "512+64, 256+64, 128+64; grouped 128+64, 128+0",
+                  s.dk, s.dr, s.dv, s.v_alias ? "latent" : "grouped");
+  } else if (s.dtype == LKV_BF16) {
     const int rows_per_kvh = s.s_q * (s.h_q / s.n_kvh);
     const bool many = s.v_alias && rows_per_kvh > 32 && lkv::mla_split_supported(s.dk, s.dr);
-    if (!many && !lkv::mfma_decode_supported(s.dk, s.dr, s.dv, s.v_alias, rows_per_kvh))
+    if (!many && !lkv::mfma_decode_supported(s.dk, s.dr, s.dv, s.v_alias, false))
       return fail(LKV_ERR_UNSUPPORTED,
                   "no bf16 kernel for key width %d + RoPE %d, value width %d (%s); compiled: latent "
                   "512+64, 256+64, 128+64, 512+0; grouped 128+64, 128+0, 64+0, 256+0",
@@ -177,6 +188,8 @@ lkv_status check_ptrs(const Shape &s, const Ptrs &p) {
       if (x && !aligned16(x)) return fail(LKV_ERR_ALIGN, "bf16 buffers must be 16-byte aligned");
     if (p.k_stride % 8 || p.v_stride % 8 || (s.dr > 0 && p.r_stride % 8))
       return fail(LKV_ERR_ALIGN, "bf16 token strides must be multiples of 8 elements");
+    if (s.fp8 && (p.k_stride % 16 || p.v_stride % 16 || (s.dr > 0 && p.r_stride % 16)))
+      return fail(LKV_ERR_ALIGN, "8-bit cache token strides must be multiples of 16 elements");
     // tile loads address 64 token rows from one base with 32-bit offsets
     if (p.k_stride > (1 << 24) || p.v_stride > (1 << 24) || p.r_stride > (1 << 24))
       return fail(LKV_ERR_SHAPE, "bf16 token strides above 2^24 elements are not supported");
@@ -228,7 +241,11 @@ lkv_status run_decode(const Shape &s, const Ptrs &p, float scale) {
   d.row_tiles = pl.row_tiles;
   d.n_chunks = pl.n_chunks;
   d.causal = s.causal ? 1 : 0;
-  d.scale_log2 = scale * 1.4426950408889634f;
+  // an 8-bit cache holds values kv_scale * code: the scores take the
+  // factor through the softmax scale, the output through its normalisation
+  d.scale_log2 = scale * (s.fp8 ? s.kv_scale : 1.f) * 1.4426950408889634f;
+  d.out_scale = s.fp8 ? s.kv_scale : 1.f;
+  d.fp8 = s.fp8 ? 1 : 0;
   d.dk = s.dk;
   d.dr = s.dr;
   d.dv = s.dv;
@@ -270,12 +287,12 @@ lkv_status run_decode(const Shape &s, const Ptrs &p, float scale) {
 
 Shape mla_shape(const lkv_mla_args *a) {
   return Shape{a->dtype, a->batch, a->s_q, a->h_q, a->n_latent, a->d_c, a->d_rope, a->d_c,
-               a->page_size, a->max_pages, a->causal, a->num_splits, true};
+               a->page_size, a->max_pages, a->causal, a->num_splits, true, a->kv_fp8 != 0, a->kv_scale};
 }
 
 Shape gqa_shape(const lkv_gqa_args *a) {
   return Shape{a->dtype, a->batch, a->s_q, a->h_q, a->n_kv, a->d_h, a->d_rope, a->d_h,
-               a->page_size, a->max_pages, a->causal, a->num_splits, false};
+               a->page_size, a->max_pages, a->causal, a->num_splits, false, a->kv_fp8 != 0, a->kv_scale};
 }
 
 }  // namespace

@@ -34,6 +34,12 @@
 //   PV:     wave w computes O^T = V^T P^T for its quarter of the value
 //           width; V^T comes straight from the token-major tile through
 //           ds_read_b64_tr_b16, P^T through LDS as bf16.
+// With an 8-bit cache (F8: OCP E4M3 codes with one dequantisation scale) the
+// next tile goes through registers instead (coalesced 16-byte loads of the
+// codes), is converted to bf16 with v_cvt_pk_f32_fp8 -- every E4M3 value is
+// exact in bf16 -- and written into the same swizzled tile layout at the end
+// of the step; the scale is folded into the softmax scale and the output
+// normalisation.  The products are unchanged.
 #include <type_traits>
 
 #include "lkv_internal.h"
@@ -180,6 +186,24 @@ __device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Four E4M3 codes (one 32-bit word) to two packed bf16 pairs: the float32
+// values are exact, so their high halves are the bf16 values.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(unsigned word) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+  const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+  return u32x2{(__float_as_uint(a[1]) & 0xffff0000u) | (__float_as_uint(a[0]) >> 16),
+               (__float_as_uint(b[1]) & 0xffff0000u) | (__float_as_uint(b[0]) >> 16)};
+}
+__device__ __forceinline__ u32x4 e4m3x8_to_u32x4(unsigned w0, unsigned w1) {
+  const u32x2 a = e4m3x4_to_bf16x4(w0), b = e4m3x4_to_bf16x4(w1);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(unsigned w0, unsigned w1) {
+  return __builtin_bit_cast(bf16x8, e4m3x8_to_u32x4(w0, w1));
+}
+
 __device__ __forceinline__ int seq_tiles(int L) { return L <= 0 ? 1 : (L + kTile - 1) / kTile; }
 
 // Split-KV plan, computed by every work-group from the device lengths: the
@@ -257,7 +281,7 @@ struct Cfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int DK, int DR, int DV, bool VA, int ROWS>
+template <int DK, int DR, int DV, bool VA, int ROWS, bool F8>
 __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodeParams p) {
   using C = Cfg<DK, DR, DV, VA, ROWS>;
   constexpr int NT = C::NT, MT = C::MT, KS = C::KS;
@@ -290,6 +314,10 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
   const bf16 *__restrict__ kc = static_cast<const bf16 *>(p.k) + (long long)kvh * DK;
   const bf16 *__restrict__ rc = static_cast<const bf16 *>(p.r);
   const bf16 *__restrict__ vc = static_cast<const bf16 *>(p.v) + (long long)kvh * DV;
+  // 8-bit cache: one byte per element
+  const char *__restrict__ kc8 = static_cast<const char *>(p.k) + (long long)kvh * DK;
+  const char *__restrict__ rc8 = static_cast<const char *>(p.r);
+  const char *__restrict__ vc8 = static_cast<const char *>(p.v) + (long long)kvh * DV;
   // a 64-token tile never straddles a page when pages are a power of two >= 64
   const bool aligned_pages = p.page_shift >= 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -405,12 +433,68 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
     const int row_first = L > 0 ? bt[0] * p.page_size : 0;
 
     // RoPE key fragments (QK^T A operand, k-steps KSN..KS-1) of this lane's
-    // token 16w + n: the current tile's and the next one's
+    // token 16w + n: the current tile's and the next one's (8-bit cache: the
+    // next one's codes, converted when they become current)
     bf16x8 rcur[C::KSR > 0 ? C::KSR : 1], rnxt[C::KSR > 0 ? C::KSR : 1];
+    u32x2 rraw[C::KSR > 0 ? C::KSR : 1];
     auto load_rope = [&](long long row, bf16x8 *dst) {
 #pragma unroll
-      for (int e = 0; e < C::KSR; ++e)
-        dst[e] = *reinterpret_cast<const bf16x8 *>(rc + row * p.r_stride + 32 * e + 8 * g);
+      for (int e = 0; e < C::KSR; ++e) {
+        if constexpr (F8)
+          rraw[e] = *reinterpret_cast<const u32x2 *>(rc8 + row * p.r_stride + 32 * e + 8 * g);
+        else
+          dst[e] = *reinterpret_cast<const bf16x8 *>(rc + row * p.r_stride + 32 * e + 8 * g);
+      }
+    };
+    auto rope_current = [&]() {
+#pragma unroll
+      for (int e = 0; e < C::KSR; ++e) {
+        if constexpr (F8) rcur[e] = e4m3x8_to_bf16x8(rraw[e][0], rraw[e][1]);
+        else rcur[e] = rnxt[e];
+      }
+    };
+
+    // 8-bit cache: the next tile's codes, 16 per thread-piece; piece q (q =
+    // tid + kThreads u) is chunk q mod (D/16) of token q / (D/16) of the key
+    // region, then of the value region
+    constexpr int NPK = kTile * DK / 16, NPV = VA ? 0 : kTile * DV / 16;
+    constexpr int NPF = F8 ? (NPK + NPV) / kThreads : 1;
+    static_assert(!F8 || (NPK % kThreads == 0 && NPV % kThreads == 0), "8-bit staging");
+    u32x4 stg[NPF];
+    auto piece = [&](int u, int &tok, int &c16) -> bool {  // true: key region
+      const int q = tid + kThreads * u;
+      const bool key = q < NPK;
+      const int qq = key ? q : q - NPK, per = (key ? DK : DV) / 16;
+      tok = qq / per;
+      c16 = qq % per;
+      return key;
+    };
+    auto load_tile8 = [&](long long row0, int rr) {
+#pragma unroll
+      for (int u = 0; u < NPF; ++u) {
+        int tok, c16;
+        const bool key = piece(u, tok, c16);
+        const long long row = row0 >= 0 ? row0 + tok : (long long)__shfl(rr, tok);
+        const char *src = key ? kc8 + row * p.k_stride : vc8 + row * p.v_stride;
+        stg[u] = *reinterpret_cast<const u32x4 *>(src + 16 * c16);
+      }
+    };
+    auto store_tile8 = [&](bf16 *buf) {
+#pragma unroll
+      for (int u = 0; u < NPF; ++u) {
+        int tok, c16;
+        const bool key = piece(u, tok, c16);
+        const u32x4 lo = e4m3x8_to_u32x4(stg[u][0], stg[u][1]);
+        const u32x4 hi = e4m3x8_to_u32x4(stg[u][2], stg[u][3]);
+        bf16 *reg = key ? buf + tok * DK : buf + C::VOFF + tok * DV;
+        if (key) {
+          *reinterpret_cast<u32x4 *>(reg + swz<DK / 8>(2 * c16, tok) * 8) = lo;
+          *reinterpret_cast<u32x4 *>(reg + swz<DK / 8>(2 * c16 + 1, tok) * 8) = hi;
+        } else {
+          *reinterpret_cast<u32x4 *>(reg + swz<DV / 8>(2 * c16, tok) * 8) = lo;
+          *reinterpret_cast<u32x4 *>(reg + swz<DV / 8>(2 * c16 + 1, tok) * 8) = hi;
+        }
+      }
     };
 
     auto load_tile = [&](int tile, bf16 *buf, bf16x8 *rdst) {
@@ -421,8 +505,12 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
         ensure_window(pi, pi);
         const int pg = __builtin_amdgcn_readlane(btw, pi - win);
         const long long row0 = (long long)pg * p.page_size + (jb & (p.page_size - 1));
-        dk_.issue(kc + row0 * p.k_stride, p.k_stride, buf, wu);
-        if constexpr (!VA) dv_.issue(vc + row0 * p.v_stride, p.v_stride, buf + C::VOFF, wu);
+        if constexpr (F8) {
+          load_tile8(row0, 0);
+        } else {
+          dk_.issue(kc + row0 * p.k_stride, p.k_stride, buf, wu);
+          if constexpr (!VA) dv_.issue(vc + row0 * p.v_stride, p.v_stride, buf + C::VOFF, wu);
+        }
         if constexpr (DR > 0) load_rope(row0 + 16 * w + n, rdst);
       } else {
         // general path: lane t computes the row of token t; tokens past the
@@ -431,8 +519,12 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
         const int j = jb + lane;
         const int pg = __shfl(btw, (page_of(j) - win) & 63);
         const int rr = j < L ? pg * p.page_size + slot_of(j) : row_first;
-        dma_region<DK / 8>(kc, p.k_stride, buf, rr, w, lane);
-        if constexpr (!VA) dma_region<DV / 8>(vc, p.v_stride, buf + C::VOFF, rr, w, lane);
+        if constexpr (F8) {
+          load_tile8(-1, rr);
+        } else {
+          dma_region<DK / 8>(kc, p.k_stride, buf, rr, w, lane);
+          if constexpr (!VA) dma_region<DV / 8>(vc, p.v_stride, buf + C::VOFF, rr, w, lane);
+        }
         if constexpr (DR > 0) load_rope(__shfl(rr, 16 * w + n), rdst);
       }
     };
@@ -441,8 +533,10 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
     // wait for them is left inside the tile loop (where it would drain the
     // prefetch of the next tile as well).
     if (L > 0) {
-      load_tile(lt0, s_buf0, rcur);
+      load_tile(lt0, s_buf0, rnxt);
       wait_vmem();
+      if constexpr (F8) store_tile8(s_buf0);
+      rope_current();
     } else {
 #pragma unroll
       for (int e = 0; e < C::KSR; ++e) rcur[e] = bf16x8{};
@@ -586,9 +680,11 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
       // unconditional: a wait that only some paths take would leave the
       // compiler assuming a load may still be in flight into the next step
       wait_vmem();
+      if constexpr (F8) {
+        if (has_next) store_tile8(nxt);
+      }
       __syncthreads();
-#pragma unroll
-      for (int e = 0; e < C::KSR; ++e) rcur[e] = rnxt[e];
+      rope_current();
     };
     for (int it = lt0; it < lt1; it += 2) {
       step(std::integral_constant<int, 0>{}, it);
@@ -610,7 +706,7 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
       float lt = 0.f;
 #pragma unroll
       for (int v = 0; v < kWaves; ++v) lt += s_red[v * ROWS + 16 * nt + n];
-      inv[nt] = lt > 0.f ? 1.f / lt : 0.f;
+      inv[nt] = lt > 0.f ? p.out_scale / lt : 0.f;
       lse_nat[nt] = lt > 0.f ? (m_run[nt] + __log2f(lt)) * kLn2 : neg_inf();
     }
     __syncthreads();
@@ -642,27 +738,27 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
   }
 }
 
-template <int DK, int DR, int DV, bool VA, int ROWS>
+template <int DK, int DR, int DV, bool VA, int ROWS, bool F8>
 hipError_t launch(const DecodeParams &p, hipStream_t s, const LaunchEvents &ev) {
   const int G = p.n_kvh * p.row_tiles;
   const int cpad = (p.n_chunks + 7) / 8 * 8;
-  return launch_timed(mfma_decode_kernel<DK, DR, DV, VA, ROWS>, dim3(G * cpad), dim3(kThreads), s, ev, p);
+  return launch_timed(mfma_decode_kernel<DK, DR, DV, VA, ROWS, F8>, dim3(G * cpad), dim3(kThreads), s, ev, p);
 }
 
-template <int DK, int DR, int DV, bool VA>
+template <int DK, int DR, int DV, bool VA, bool F8>
 hipError_t launch_rows(const DecodeParams &p, int rows, hipStream_t s, const LaunchEvents &ev) {
-  return rows == 16 ? launch<DK, DR, DV, VA, 16>(p, s, ev) : launch<DK, DR, DV, VA, 32>(p, s, ev);
+  return rows == 16 ? launch<DK, DR, DV, VA, 16, F8>(p, s, ev) : launch<DK, DR, DV, VA, 32, F8>(p, s, ev);
 }
 
 // Work-groups of one instantiation resident on a CU at once (registers and
 // LDS), queried once per instantiation; 1 if the query fails.
-template <int DK, int DR, int DV, bool VA, int ROWS>
+template <int DK, int DR, int DV, bool VA, int ROWS, bool F8>
 int blocks_per_cu() {
   static int cached = 0;  // the same for every gfx950 device
   if (cached == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mfma_decode_kernel<DK, DR, DV, VA, ROWS>, kThreads, 0) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mfma_decode_kernel<DK, DR, DV, VA, ROWS, F8>, kThreads,
+                                                     0) != hipSuccess ||
         n < 1)
       n = 1;
     cached = n;
@@ -684,29 +780,56 @@ int mfma_decode_rows(int rows_per_kvh) { return rows_per_kvh <= 16 ? 16 : 32; }
   X(128, 0, 128, false)        \
   X(64, 0, 64, false)          \
   X(256, 0, 256, false)
+// ... and those with an 8-bit (E4M3) cache
+#define LKV_MFMA_F8_VARIANTS(X) \
+  X(512, 64, 512, true)         \
+  X(256, 64, 256, true)         \
+  X(128, 64, 128, true)         \
+  X(128, 64, 128, false)        \
+  X(128, 0, 128, false)
 
-bool mfma_decode_supported(int dk, int dr, int dv, bool v_alias, int) {
+bool mfma_decode_supported(int dk, int dr, int dv, bool v_alias, bool fp8) {
 #define LKV_SUP(DK, DR, DV, VA) \
   if (dk == DK && dr == DR && dv == DV && v_alias == VA) return true;
-  LKV_MFMA_VARIANTS(LKV_SUP)
+  if (fp8) {
+    LKV_MFMA_F8_VARIANTS(LKV_SUP)
+  } else {
+    LKV_MFMA_VARIANTS(LKV_SUP)
+  }
 #undef LKV_SUP
   return false;
 }
 
-int mfma_decode_blocks_per_cu(int dk, int dr, int dv, bool v_alias, int rows) {
-#define LKV_OCC(DK, DR, DV, VA)                                   \
+int mfma_decode_blocks_per_cu(int dk, int dr, int dv, bool v_alias, int rows, bool fp8) {
+#define LKV_OCC(DK, DR, DV, VA, F8)                               \
   if (dk == DK && dr == DR && dv == DV && v_alias == VA)          \
-    return rows == 16 ? blocks_per_cu<DK, DR, DV, VA, 16>() : blocks_per_cu<DK, DR, DV, VA, 32>();
-  LKV_MFMA_VARIANTS(LKV_OCC)
+    return rows == 16 ? blocks_per_cu<DK, DR, DV, VA, 16, F8>() : blocks_per_cu<DK, DR, DV, VA, 32, F8>();
+#define LKV_OCC16(DK, DR, DV, VA) LKV_OCC(DK, DR, DV, VA, false)
+#define LKV_OCC8(DK, DR, DV, VA) LKV_OCC(DK, DR, DV, VA, true)
+  if (fp8) {
+    LKV_MFMA_F8_VARIANTS(LKV_OCC8)
+  } else {
+    LKV_MFMA_VARIANTS(LKV_OCC16)
+  }
+#undef LKV_OCC8
+#undef LKV_OCC16
 #undef LKV_OCC
   return 1;
 }
 
 hipError_t launch_mfma_decode(const DecodeParams &p, bool v_alias, int rows, hipStream_t s,
                               const LaunchEvents &ev) {
-#define LKV_DISPATCH(DK, DR, DV, VA) \
-  if (p.dk == DK && p.dr == DR && p.dv == DV && v_alias == VA) return launch_rows<DK, DR, DV, VA>(p, rows, s, ev);
-  LKV_MFMA_VARIANTS(LKV_DISPATCH)
+#define LKV_DISPATCH(DK, DR, DV, VA, F8) \
+  if (p.dk == DK && p.dr == DR && p.dv == DV && v_alias == VA) return launch_rows<DK, DR, DV, VA, F8>(p, rows, s, ev);
+#define LKV_DISPATCH16(DK, DR, DV, VA) LKV_DISPATCH(DK, DR, DV, VA, false)
+#define LKV_DISPATCH8(DK, DR, DV, VA) LKV_DISPATCH(DK, DR, DV, VA, true)
+  if (p.fp8) {
+    LKV_MFMA_F8_VARIANTS(LKV_DISPATCH8)
+  } else {
+    LKV_MFMA_VARIANTS(LKV_DISPATCH16)
+  }
+#undef LKV_DISPATCH8
+#undef LKV_DISPATCH16
 #undef LKV_DISPATCH
   return hipErrorInvalidValue;
 }

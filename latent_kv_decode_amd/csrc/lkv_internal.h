@@ -52,7 +52,10 @@ struct DecodeParams {
   int row_tiles;               // ceil(rows_per_kvh / ROWS)
   int n_chunks;                // split-KV shares of the concatenated tiles
   int causal;
-  float scale_log2;            // softmax scale * log2(e)
+  float scale_log2;            // softmax scale * log2(e) (times the cache scale)
+  float out_scale;             // factor on the normalised output: the cache's
+                               // dequantisation scale (8-bit cache), else 1
+  int fp8;                     // the caches hold OCP E4M3 codes (row-tiled kernel)
   int dk, dr, dv;              // widths (used by the generic fp32 kernel)
 };
 
@@ -97,11 +100,11 @@ struct ExpandParams {
 // Launchers return hipSuccess or the launch error.  `bf16_variant` selects a
 // compiled instantiation; launchers return hipErrorInvalidValue when none
 // matches (the ABI checks support before calling).
-bool mfma_decode_supported(int dk, int dr, int dv, bool v_alias, int rows_per_kvh);
+bool mfma_decode_supported(int dk, int dr, int dv, bool v_alias, bool fp8);
 int mfma_decode_rows(int rows_per_kvh);  // ROWS template used for this problem
 // Work-groups of the instantiation for (dk, dr, dv, v_alias, rows) that fit
 // on one CU at once.
-int mfma_decode_blocks_per_cu(int dk, int dr, int dv, bool v_alias, int rows);
+int mfma_decode_blocks_per_cu(int dk, int dr, int dv, bool v_alias, int rows, bool fp8);
 hipError_t launch_mfma_decode(const DecodeParams &p, bool v_alias, int rows, hipStream_t s,
                               const LaunchEvents &ev);
 // Latent path with the score and value products on different waves, 64 query

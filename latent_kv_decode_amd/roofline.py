@@ -11,7 +11,8 @@ a kernel does it:
 Per-token figures follow the GQLA explainer (technical summary sections 2
 and 4): the MQA-absorbed path keeps r_kv + d^R_h elements per token and does
 h_q*(2*(d_c + d_rope) + 2*d_c) FLOPs per cache token per query token; the GQA
-path keeps 2*g*d_h + d^R_h elements per token.
+path keeps 2*g*d_h + d^R_h elements per token.  An 8-bit cache (cache_elem =
+1) halves the cache bytes; query and output stay 2 bytes per element.
 """
 from __future__ import annotations
 
@@ -72,9 +73,9 @@ def _visible(L: int, s_q: int, t: int, causal: bool) -> int:
 
 
 def mla_work(seqlens, *, s_q: int, h_q: int, n_lat: int, d_c: int, d_rope: int, page_size: int,
-             causal: bool = True, elem: int = 2) -> Work:
+             causal: bool = True, elem: int = 2, cache_elem: int | None = None) -> Work:
     tok = sum(int(L) for L in seqlens)
-    cache = tok * (n_lat * d_c + d_rope) * elem
+    cache = tok * (n_lat * d_c + d_rope) * (elem if cache_elem is None else cache_elem)
     B = len(seqlens)
     rows = B * s_q * h_q
     q = rows * (d_c + d_rope) * elem
@@ -87,9 +88,9 @@ def mla_work(seqlens, *, s_q: int, h_q: int, n_lat: int, d_c: int, d_rope: int, 
 
 
 def gqa_work(seqlens, *, s_q: int, h_q: int, n_kv: int, d_h: int, d_rope: int, page_size: int,
-             causal: bool = True, elem: int = 2) -> Work:
+             causal: bool = True, elem: int = 2, cache_elem: int | None = None) -> Work:
     tok = sum(int(L) for L in seqlens)
-    cache = tok * (2 * n_kv * d_h + d_rope) * elem
+    cache = tok * (2 * n_kv * d_h + d_rope) * (elem if cache_elem is None else cache_elem)
     B = len(seqlens)
     rows = B * s_q * h_q
     q = rows * (d_h + d_rope) * elem

@@ -52,6 +52,31 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return out
 
 
+# OCP 8-bit float E4M3 ("fn": no infinities; S.1111.111 is NaN), the
+# positive codes 0x00..0x7E in increasing order of value
+E4M3_NAN = np.uint8(0x7F)
+
+
+def _e4m3_positive_values() -> np.ndarray:
+    codes = np.arange(0x7F)
+    e, m = codes >> 3, codes & 7
+    return np.where(e == 0, m * 2.0 ** -9, (8 + m) * 2.0 ** (e - 10.0))
+
+
+def to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round float values to OCP E4M3 codes: nearest, ties to the even code;
+    magnitudes beyond 448 saturate to 448; NaN to 0x7F."""
+    x = np.asarray(x, dtype=np.float64)
+    vals = _e4m3_positive_values()
+    a = np.minimum(np.abs(x), vals[-1])
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, vals.size - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - vals[lo], vals[hi] - a
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = pick.astype(np.uint8) | np.where(np.signbit(x), np.uint8(0x80), np.uint8(0))
+    return np.where(np.isnan(x), E4M3_NAN, code).astype(np.uint8)
+
+
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b).astype(np.uint32) << 16).view(np.float32)
 
@@ -164,6 +189,10 @@ class Workload:
     table: str = "shuffled"
     max_pages: int | None = None
     causal: bool = True
+    # '' = the cache holds the input dtype; 'fp8' = OCP E4M3 codes x8 of
+    # values kv_scale * x8 (one scale for the whole cache)
+    cache: str = ""
+    kv_scale: float = 1.0 / 16
     scale: float = 0.0
     seed: int = 0
     note: str = ""
@@ -236,6 +265,9 @@ WORKLOADS = {
                              seqlens=(8192,) * 64, table="shuffled", scale=1 / math.sqrt(128),
                              seed=9),
 }
+# 8-bit (OCP E4M3) caches of the same draws, one scale per cache
+for _n in ("dsv3_mla_b64_l4096", "gla2_b128_l8192", "gqa_b128_l8192"):
+    WORKLOADS[_n + "_fp8"] = replace(WORKLOADS[_n], name=_n + "_fp8", cache="fp8")
 
 
 def workload(name: str, **overrides) -> Workload:
@@ -301,6 +333,21 @@ def generate(w: Workload, *, poison: bool = True, seqlens=None) -> dict:
         invalid = ~valid_slot_mask(table, sl, P, num_pages)
         for c in caches:
             c[invalid] = _nan_of(dt)
+    if w.cache == "fp8":
+        # the same draws, stored as E4M3 codes of value / kv_scale
+        keys = ["kv"] if w.kind in ("mla", "gqla") else ["k_cache", "v_cache"] + (
+            ["k_rope"] if w.d_rope else [])
+        if dt == "bf16":
+            # every bf16 pattern through the encoder once, then a lookup
+            allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+            with np.errstate(invalid="ignore"):  # signalling-NaN patterns
+                lut = to_e4m3_bits(bf16_bits_to_f32(allbits).astype(np.float64) / w.kv_scale)
+        for k in keys:
+            if dt == "bf16":
+                out[k] = lut[out[k]]
+            else:
+                out[k] = to_e4m3_bits(out[k].astype(np.float64) / w.kv_scale)
+        out["kv_scale"] = w.kv_scale
     return out
 
 

@@ -336,3 +336,16 @@ def append_tokens(src, cache, block_table, seqlens, *, page_size, tok_stride):
             row = int(block_table[b, j // page_size]) * page_size + j % page_size
             out[row * tok_stride: row * tok_stride + width] = src[b, t]
     return out
+
+
+
+def e4m3_to_f64(codes, scale=1.0):
+    """Values of OCP 8-bit float E4M3 codes times ``scale`` (the "fn" variant:
+    sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0
+    holds the subnormals m * 2^-9; S.1111.111 is NaN; no infinities)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s, e, m = c >> 7, (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    v = np.where(s == 1, -mag, mag)
+    v = np.where((e == 15) & (m == 7), np.nan, v)
+    return v * scale

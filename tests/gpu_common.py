@@ -95,15 +95,30 @@ def oracle_mla(oracle, w, x, rows=None, q_nope=None):
 
 
 def small_mla(seed, *, B=3, h_q=128, s_q=1, n_lat=1, d_c=512, d_rope=64, page=64, seqlens=None,
-              table="fragmented", causal=True, dtype="bf16", max_pages=None):
+              table="fragmented", causal=True, dtype="bf16", max_pages=None, cache=""):
     rng = np.random.default_rng(seed)
     if seqlens is None:
         seqlens = rng.integers(s_q, 700, size=B)
     w = li.Workload(name=f"small{seed}", kind="mla", dtype=dtype, B=len(seqlens), h_q=h_q, s_q=s_q,
                     page_size=page, n_lat=n_lat, d_c=d_c, d_rope=d_rope,
                     seqlens=tuple(int(v) for v in seqlens), table=table, causal=causal,
-                    max_pages=max_pages, scale=1 / math.sqrt(d_c + d_rope), seed=seed)
+                    max_pages=max_pages, scale=1 / math.sqrt(d_c + d_rope), seed=seed,
+                    cache=cache)
     return w, li.generate(w)
+
+
+def dequantised(oracle, x, cache_keys, q_keys):
+    """Copy of generate()'s output for the oracle when the caches hold E4M3
+    codes: caches as float32 values through the oracle's decoding of all 256
+    codes (exact: the scale is a power of two), bf16 queries widened to
+    float32 so that every oracle input shares one dtype."""
+    lut = oracle.e4m3_to_f64(np.arange(256, dtype=np.uint8), x["kv_scale"]).astype(np.float32)
+    y = dict(x)
+    for k in cache_keys:
+        y[k] = lut[x[k]]
+    for k in q_keys:
+        y[k] = li.bf16_bits_to_f32(x[k])
+    return y
 
 
 def rows_of(out, rows):

@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert lkv.lkv_abi_version() == 1
+    assert lkv.lkv_abi_version() == 2
 
 
 def _c_layout(struct, fields):
@@ -111,6 +111,12 @@ def _status(lib, a):
     (dict(softmax_scale=-0.05), 2),
     (dict(softmax_scale=float("inf")), 2),
     (dict(softmax_scale=float("nan")), 2),
+    # 8-bit cache
+    (dict(kv_fp8=1, kv_scale=0.0), 2),
+    (dict(kv_fp8=1, kv_scale=float("nan")), 2),
+    (dict(kv_fp8=1, kv_scale=0.1, dtype=0), 3),
+    (dict(kv_fp8=1, kv_scale=0.1, d_rope=0), 3),
+    (dict(kv_fp8=1, kv_scale=0.1, kv_tok_stride=584, rope_tok_stride=584), 4),
 ])
 def test_mla_validation(lib, change, expect):
     st = _status(lib, _mla(**change))

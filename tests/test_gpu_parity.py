@@ -13,8 +13,8 @@ import numpy as np
 import pytest
 
 import lkv_inputs as li
-from tests.gpu_common import (assert_close, from_dev, mla_device_inputs, note, oracle_mla,
-                              rows_of, run_mla, small_mla, to_dev)
+from tests.gpu_common import (assert_close, dequantised, from_dev, mla_device_inputs, note,
+                              oracle_mla, rows_of, run_mla, small_mla, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -259,10 +259,11 @@ def test_page_permutation_and_repeat_bit_identical(lkv):
 
 # ------------------------------------------------------------------ GQA path
 def _gqa_small(seed, *, B=3, h_q=32, n_kv=8, d_h=128, d_rope=0, s_q=1, seqlens=(100, 700, 65),
-               causal=True):
-    w = li.Workload(name="g", kind="gqa", dtype="bf16", B=B, h_q=h_q, s_q=s_q, page_size=64,
-                    n_kv=n_kv, d_h=d_h, d_rope=d_rope, seqlens=tuple(seqlens), table="shuffled",
-                    causal=causal, scale=1 / math.sqrt(d_h + d_rope), seed=seed)
+               causal=True, page=64, cache=""):
+    w = li.Workload(name="g", kind="gqa", dtype="bf16", B=len(seqlens), h_q=h_q, s_q=s_q,
+                    page_size=page, n_kv=n_kv, d_h=d_h, d_rope=d_rope, seqlens=tuple(seqlens),
+                    table="shuffled", causal=causal, scale=1 / math.sqrt(d_h + d_rope),
+                    seed=seed, cache=cache)
     return w, li.generate(w)
 
 
@@ -500,6 +501,83 @@ def test_split_combine_entry_point(lkv, oracle):
                      what=f"combine {dt}")
 
 
+# ------------------------------------------------------------ 8-bit caches
+# The caches hold OCP E4M3 codes of value / kv_scale; the oracle sees the
+# dequantised values (float32, exact) and float32 copies of the bf16 queries.
+GQA_KEYS = ["k_cache", "v_cache"]
+
+
+def _fp8(w):
+    return dict(kv_fp8=True, kv_scale=w.kv_scale)
+
+
+@pytest.mark.parametrize("h_q,n_kv,d_h,d_rope,s_q,splits,page,seqlens", [
+    (32, 8, 128, 0, 1, 0, 64, (100, 700, 65)),
+    (128, 8, 128, 64, 2, 0, 64, (100, 700, 65)),     # GQLA grouped, g = 8
+    (128, 8, 128, 64, 2, 7, 64, (100, 700, 65)),
+    (128, 2, 128, 0, 1, 0, 64, (0, 1, 130, 64)),    # GQA-2; empty and 1-token rows
+    (8, 1, 128, 0, 2, 3, 48, (100, 700, 65)),       # general pages
+    (32, 8, 128, 64, 1, 0, 16, (333, 64, 1000))])
+def test_gqa_fp8(lkv, oracle, h_q, n_kv, d_h, d_rope, s_q, splits, page, seqlens):
+    w, x = _gqa_small(900 + h_q + page + splits, h_q=h_q, n_kv=n_kv, d_h=d_h, d_rope=d_rope,
+                      s_q=s_q, page=page, seqlens=seqlens, cache="fp8")
+    assert x["k_cache"].dtype == np.uint8
+    note(f"case gqa fp8 h_q={h_q} n_kv={n_kv} d_rope={d_rope} s_q={s_q} splits={splits} "
+         f"page={page} seqlens={seqlens}")
+    out, lse = _run_gqa(lkv, w, x, num_splits=splits, **_fp8(w))
+    keys = GQA_KEYS + (["k_rope"] if d_rope else [])
+    y = dequantised(oracle, x, keys, ["q"] + (["q_rope"] if d_rope else []))
+    ro, rl = _oracle_gqa(oracle, w, y)
+    assert_close(from_dev(out), ro, from_dev(lse), rl, what="gqa fp8")
+
+
+@pytest.mark.parametrize("h_q,n_lat,d_c,s_q,splits,page,seqlens", [
+    (16, 1, 512, 1, 0, 64, (70, 600, 129, 1)),      # few-head MLA
+    (128, 1, 512, 1, 0, 64, (70, 600, 129, 1)),     # many-row MLA
+    (128, 1, 512, 2, 5, 48, (70, 600, 129, 2)),
+    (32, 2, 256, 1, 0, 64, (0, 300, 1000)),         # GLA-2
+    (32, 2, 256, 2, 3, 32, (64, 300, 1000)),
+    (32, 8, 128, 1, 0, 64, (500, 65, 128))])        # GTA
+def test_mla_fp8(lkv, oracle, h_q, n_lat, d_c, s_q, splits, page, seqlens):
+    w, x = small_mla(950 + h_q + d_c + s_q + page, h_q=h_q, n_lat=n_lat, d_c=d_c, s_q=s_q,
+                     page=page, seqlens=seqlens, cache="fp8")
+    assert x["kv"].dtype == np.uint8
+    note(f"case mla fp8 h_q={h_q} n_lat={n_lat} d_c={d_c} s_q={s_q} splits={splits} page={page} "
+         f"seqlens={seqlens}")
+    d = mla_device_inputs(x, w, torch)
+    out, lse = run_mla(lkv, w, d, x=x, num_splits=splits, **_fp8(w))
+    ro, rl = oracle_mla(oracle, w, dequantised(oracle, x, ["kv"], ["q_nope", "q_rope"]))
+    assert_close(from_dev(out), ro, from_dev(lse), rl, what="mla fp8")
+
+
+@pytest.mark.parametrize("kind", ["gqa", "gla2", "mla16"])
+def test_fp8_equals_bf16_of_dequantised_cache(lkv, oracle, kind):
+    """With a power-of-two kv_scale every scaling is exact, so the 8-bit path
+    must give the bits of the bf16 path over the dequantised cache (same
+    kernel, same split plan)."""
+    if kind == "gqa":
+        w, x = _gqa_small(990, h_q=128, n_kv=8, d_rope=64, s_q=2, cache="fp8")
+        keys = GQA_KEYS + ["k_rope"]
+    else:
+        h_q, n_lat, d_c = (32, 2, 256) if kind == "gla2" else (16, 1, 512)
+        w, x = small_mla(991, h_q=h_q, n_lat=n_lat, d_c=d_c, seqlens=(70, 600, 129), cache="fp8")
+        keys = ["kv"]
+    note(f"case fp8 == bf16 of dequantised cache, {kind}")
+    lut = li.to_bf16_bits(oracle.e4m3_to_f64(np.arange(256, dtype=np.uint8), w.kv_scale))
+    xb = dict(x)
+    for k in keys:
+        xb[k] = lut[x[k]]
+    if kind == "gqa":
+        o8, l8 = _run_gqa(lkv, w, x, num_splits=4, **_fp8(w))
+        ob, lb = _run_gqa(lkv, w, xb, num_splits=4)
+    else:
+        o8, l8 = run_mla(lkv, w, mla_device_inputs(x, w, torch), x=x, num_splits=4, **_fp8(w))
+        ob, lb = run_mla(lkv, w, mla_device_inputs(xb, w, torch), x=xb, num_splits=4)
+    torch.cuda.synchronize()
+    assert torch.equal(o8.view(torch.int16), ob.view(torch.int16))
+    assert torch.equal(l8, lb)
+
+
 # ------------------------------------------------------- full-size workloads
 FULL = [("dsv3_mla_b64_l4096", 96), ("gla2_b128_l8192", 64), ("ragged_mla_b16_sq1", 48),
         ("ragged_mla_b16_sq2", 48), ("mtp_mla_b64_l4096_sq4", 64), ("gta_b128_l8192", 64)]
@@ -535,6 +613,30 @@ def test_full_size_gqa_sampled(lkv, oracle, name):
     assert np.isfinite(got).all()
     assert_close(rows_of(got, rows), rows_of(ro, rows), rows_of(gl, rows), rows_of(rl, rows),
                  what=f"{name} full")
+
+
+@pytest.mark.parametrize("name,nrows", [("dsv3_mla_b64_l4096_fp8", 64),
+                                        ("gla2_b128_l8192_fp8", 48), ("gqa_b128_l8192_fp8", 48)])
+def test_full_size_fp8_sampled(lkv, oracle, name, nrows):
+    w = li.workload(name)
+    note(f"case full {name}: generating inputs")
+    x = li.generate(w)
+    note(f"case full {name}: running GPU")
+    if w.kind == "gqa":
+        out, lse = _run_gqa(lkv, w, x, **_fp8(w))
+    else:
+        out, lse = run_mla(lkv, w, mla_device_inputs(x, w, torch), x=x, **_fp8(w))
+    torch.cuda.synchronize()
+    rows = li.sample_rows(14, w.B, w.s_q, w.h_q, nrows)
+    if w.kind == "gqa":
+        ro, rl = _oracle_gqa(oracle, w, dequantised(oracle, x, GQA_KEYS, ["q"]), rows=rows)
+    else:
+        ro, rl = oracle_mla(oracle, w, dequantised(oracle, x, ["kv"], ["q_nope", "q_rope"]),
+                            rows=rows)
+    got, gl = from_dev(out), from_dev(lse)
+    assert np.isfinite(got).all() and np.isfinite(gl).all()
+    assert_close(rows_of(got, rows), rows_of(ro, rows), rows_of(gl, rows), rows_of(rl, rows),
+                 what=name)
 
 
 @pytest.mark.parametrize("name", ["gqla_grouped_b64_l4096_sq2", "gqla_g4_b64_l4096_sq1"])

@@ -443,3 +443,23 @@ def test_append_tokens_rebuilds_the_generated_cache(oracle_lib):
     valid = li.valid_slot_mask(bt, sl, P, npg)
     assert np.array_equal(got[valid], kv[valid])
     assert (got[~valid] == sentinel).all()
+
+
+def test_e4m3_decode_matches_the_format_definition(oracle_lib):
+    """OCP E4M3 values fixed by the format: 1.0, the largest normal 448, the
+    smallest normal 2^-6, the smallest subnormal 2^-9, the largest subnormal
+    7 * 2^-9, signed zero, NaN; and the input generator's encoder is the
+    inverse of the decoder on every finite code."""
+    f = oracle_lib.e4m3_to_f64
+    fixed = {0x38: 1.0, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9,
+             0x00: 0.0, 0xB8: -1.0, 0xFE: -448.0, 0x40: 2.0, 0x3C: 1.5}
+    for code, val in fixed.items():
+        assert f(np.array([code]))[0] == val, hex(code)
+    assert np.isnan(f(np.array([0x7F, 0xFF]))).all()
+    assert np.signbit(f(np.array([0x80]))[0])
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    assert np.array_equal(li.to_e4m3_bits(f(codes)), codes)
+    # rounding: halfway between 1.0 (0x38) and 1.125 (0x39) goes to the even code
+    assert li.to_e4m3_bits(np.array([1.0625]))[0] == 0x38
+    assert li.to_e4m3_bits(np.array([1.1875]))[0] == 0x3A
+    assert li.to_e4m3_bits(np.array([1000.0]))[0] == 0x7E

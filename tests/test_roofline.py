@@ -67,6 +67,19 @@ def test_work_counts_headline_workload():
     assert abs(w.intensity - 228.3) < 0.5
 
 
+def test_work_counts_8bit_cache():
+    """An E4M3 cache is one byte per element; query, output, LSE and metadata
+    keep their sizes, and the FLOPs do not change."""
+    w2 = rf.mla_work([4096] * 64, s_q=1, h_q=128, n_lat=1, d_c=512, d_rope=64, page_size=64)
+    w1 = rf.mla_work([4096] * 64, s_q=1, h_q=128, n_lat=1, d_c=512, d_rope=64, page_size=64,
+                     cache_elem=1)
+    assert w1.cache_bytes == 64 * 4096 * 576
+    assert w2.bytes - w1.bytes == w1.cache_bytes and w1.flops == w2.flops
+    g = rf.gqa_work([8192] * 128, s_q=1, h_q=32, n_kv=8, d_h=128, d_rope=0, page_size=64,
+                    cache_elem=1)
+    assert g.cache_bytes == 128 * 8192 * 2 * 8 * 128
+
+
 def test_work_counts_causal_sq2():
     w1 = rf.mla_work([10], s_q=2, h_q=1, n_lat=1, d_c=4, d_rope=0, page_size=4)
     assert w1.flops == (9 + 10) * (2 * 4 + 2 * 4)
