@@ -215,8 +215,7 @@ def setup_mla(w, x, args, torch, lkv, rf):
     work = rf.mla_work(x["seqlens"], s_q=w.s_q, h_q=w.h_q, n_lat=w.n_lat, d_c=w.d_c,
                        d_rope=w.d_rope, page_size=w.page_size, causal=w.causal,
                        cache_elem=1 if fp8 else 2)
-    # the many-row split kernel reads bf16 caches only
-    many_rows = w.h_q // w.n_lat * w.s_q > 32 and w.d_c in (256, 512) and not fp8
+    many_rows = w.h_q // w.n_lat * w.s_q > 32 and w.d_c in (256, 512)
     return dict(step=step, work=work, parity=parity, cpu=cpu,
                 kernel="mla_split_kernel" if many_rows else "mfma_decode_kernel",
                 config={"n_latent": w.n_lat, "d_c": w.d_c, "d_rope": w.d_rope,

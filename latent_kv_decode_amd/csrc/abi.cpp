@@ -89,7 +89,7 @@ lkv_status make_plan(const Shape &s, Plan *pl) {
   // Many query rows over one latent: one work-group takes 64 of them and
   // reads each cache tile once for all of them.
   pl->latent = kLatentNone;
-  if (s.dtype == LKV_BF16 && !s.fp8 && s.v_alias && rows_per_kvh > 32 && lkv::mla_split_supported(s.dk, s.dr))
+  if (s.dtype == LKV_BF16 && s.v_alias && rows_per_kvh > 32 && lkv::mla_split_supported(s.dk, s.dr))
     pl->latent = kLatentSplit;
   pl->rows = pl->latent == kLatentSplit ? lkv::mla_split_rows() : lkv::mfma_decode_rows(rows_per_kvh);
   pl->row_tiles = (rows_per_kvh + pl->rows - 1) / pl->rows;
@@ -142,7 +142,9 @@ lkv_status check_shape(const Shape &s) {
     if (s.dtype != LKV_BF16) return fail(LKV_ERR_UNSUPPORTED, "an 8-bit cache needs bf16 queries and output");
     if (!(s.kv_scale > 0.f) || !std::isfinite(s.kv_scale))
       return fail(LKV_ERR_SHAPE, "kv_scale %g must be positive and finite", (double)s.kv_scale);
-    if (!lkv::mfma_decode_supported(s.dk, s.dr, s.dv, s.v_alias, true))
+    const int rows_per_kvh = s.s_q * (s.h_q / s.n_kvh);
+    const bool many = s.v_alias && rows_per_kvh > 32 && lkv::mla_split_supported(s.dk, s.dr);
+    if (!many && !lkv::mfma_decode_supported(s.dk, s.dr, s.dv, s.v_alias, true))
       return fail(LKV_ERR_UNSUPPORTED,
                   "no 8-bit-cache kernel for key width %d + RoPE %d, value width %d (%s); compiled: latent "
                   "512+64, 256+64, 128+64; grouped 128+64, 128+0",

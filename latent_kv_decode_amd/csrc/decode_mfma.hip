@@ -42,6 +42,7 @@
 // normalisation.  The products are unchanged.
 #include <type_traits>
 
+#include "e4m3.h"
 #include "lkv_internal.h"
 
 namespace lkv {
@@ -186,22 +187,9 @@ __device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Four E4M3 codes (one 32-bit word) to two packed bf16 pairs: the float32
-// values are exact, so their high halves are the bf16 values.
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(unsigned word) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-  const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-  return u32x2{(__float_as_uint(a[1]) & 0xffff0000u) | (__float_as_uint(a[0]) >> 16),
-               (__float_as_uint(b[1]) & 0xffff0000u) | (__float_as_uint(b[0]) >> 16)};
-}
-__device__ __forceinline__ u32x4 e4m3x8_to_u32x4(unsigned w0, unsigned w1) {
-  const u32x2 a = e4m3x4_to_bf16x4(w0), b = e4m3x4_to_bf16x4(w1);
-  return u32x4{a[0], a[1], b[0], b[1]};
-}
+typedef e4m3_u32x2 u32x2;
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(unsigned w0, unsigned w1) {
-  return __builtin_bit_cast(bf16x8, e4m3x8_to_u32x4(w0, w1));
+  return __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8_bits(w0, w1));
 }
 
 __device__ __forceinline__ int seq_tiles(int L) { return L <= 0 ? 1 : (L + kTile - 1) / kTile; }
@@ -484,8 +472,8 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
       for (int u = 0; u < NPF; ++u) {
         int tok, c16;
         const bool key = piece(u, tok, c16);
-        const u32x4 lo = e4m3x8_to_u32x4(stg[u][0], stg[u][1]);
-        const u32x4 hi = e4m3x8_to_u32x4(stg[u][2], stg[u][3]);
+        const u32x4 lo = e4m3x8_to_bf16x8_bits(stg[u][0], stg[u][1]);
+        const u32x4 hi = e4m3x8_to_bf16x8_bits(stg[u][2], stg[u][3]);
         bf16 *reg = key ? buf + tok * DK : buf + C::VOFF + tok * DV;
         if (key) {
           *reinterpret_cast<u32x4 *>(reg + swz<DK / 8>(2 * c16, tok) * 8) = lo;

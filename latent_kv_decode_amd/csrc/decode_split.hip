@@ -21,8 +21,16 @@
 // by direct-to-LDS buffer loads into a ring of four buffers, two tiles ahead;
 // the value waves issue their share of a tile before their products, the
 // score waves after theirs.
+//
+// 8-bit (E4M3) cache: the score waves load a tile's codes into registers one
+// iteration before it is needed (two register sets), convert them to bf16 and
+// write them in the same ring slot layout, so the products read bf16 as
+// above.  Each code is converted once per work-group; the cache bytes read
+// are halved.  The value waves, whose accumulators fill their registers, do
+// no staging.
 #include <type_traits>
 
+#include "e4m3.h"
 #include "lkv_internal.h"
 
 namespace lkv {
@@ -197,7 +205,7 @@ struct SCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int DK, int DR>
+template <int DK, int DR, bool F8>
 __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodeParams p) {
   using C = SCfg<DK, DR>;
   constexpr int KS = C::KS, KSN = C::KSN, MTV = C::MTV, CPT = C::CPT, NLL = C::NLL;
@@ -231,9 +239,11 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
 
   const bf16 *__restrict__ qn = static_cast<const bf16 *>(p.q);
   const bf16 *__restrict__ qr_ = static_cast<const bf16 *>(p.q_rope);
-  const char *kcb = reinterpret_cast<const char *>(static_cast<const bf16 *>(p.k) + (long long)kvh * DK);
+  // cache element size: 1 byte (E4M3 code) or 2 (bf16)
+  constexpr int ES = F8 ? 1 : 2;
+  const char *kcb = static_cast<const char *>(p.k) + (long long)kvh * DK * ES;
   const char *rcb = static_cast<const char *>(p.r);
-  const long long kstr = p.k_stride * 2, rstr = p.r_stride * 2;
+  const long long kstr = p.k_stride * ES, rstr = p.r_stride * ES;
   const bool aligned_pages = p.page_shift >= 5;
 
   // The two roles run the same loop (same tiles, same barriers); each is
@@ -271,7 +281,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
     for (int e = 0; e < 2; ++e) lofs[e] = swz<CPT>(lane % CPT, kWaves * e + wu) * 16;
     if constexpr (kScore && DR > 0) rofs = (int)((lane >> 3) * rstr) + swz<8>(lane & 7, 8 * sw + (lane >> 3)) * 16;
 
-    {
+    if constexpr (!F8) {
       // One empty-range load (no memory access) into each ring buffer in
       // ring order, ahead of every path: the compiler's wait placement tracks
       // direct-to-LDS loads per buffer in order of first use, and a common
@@ -419,6 +429,57 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
         for (int i = tid; i < C::BUF / 8; i += kThreads) *reinterpret_cast<u32x4 *>(buf + 8 * i) = u32x4{0u, 0u, 0u, 0u};
       };
 
+      // 8-bit cache staging (score waves).  Piece q = lane + 64 i of score
+      // wave sw (16 codes) is chunk q mod PPR of latent row 4 (q / PPR) + sw
+      // of the tile; lanes 0..31 also stage RoPE row 8 sw + lane / 4, chunk
+      // lane mod 4.  Tiles past the share (dma_range == 0) read nothing and
+      // stage zeros.
+      constexpr int PPR = DK / 16;
+      constexpr int NPL = F8 && kScore ? 8 * PPR / 64 : 0;
+      constexpr bool kRopeStage = F8 && kScore && DR > 0;
+      static_assert(!F8 || 8 * PPR % 64 == 0, "8-bit staging");
+      u32x4 stg[2][NPL + 1];
+      auto row_of = [&](int t) -> long long {
+        return dma_al ? (long long)__builtin_amdgcn_readlane(dma_rows, 0) + t : (long long)__shfl(dma_rows, t);
+      };
+      // S: register set (compile time, so that the sets stay in registers)
+      auto stage_load = [&](auto s_tag) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_tag)::value;
+        if (dma_range != 0) {
+#pragma unroll
+          for (int i = 0; i < NPL; ++i) {
+            const int q = lane + 64 * i, t = 4 * (q / PPR) + sw;
+            stg[S][i] = *reinterpret_cast<const u32x4 *>(kcb + row_of(t) * kstr + 16 * (q % PPR));
+          }
+          if constexpr (kRopeStage) {
+            stg[S][NPL] = u32x4{0u, 0u, 0u, 0u};
+            if (lane < 32)
+              stg[S][NPL] = *reinterpret_cast<const u32x4 *>(rcb + row_of(8 * sw + (lane >> 2)) * rstr + 16 * (lane & 3));
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i <= NPL; ++i) stg[S][i] = u32x4{0u, 0u, 0u, 0u};
+        }
+      };
+      auto stage_store = [&](auto s_tag, bf16 *buf) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_tag)::value;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+          const int q = lane + 64 * i, t = 4 * (q / PPR) + sw, c16 = q % PPR;
+          bf16 *row = buf + t * DK;
+          *reinterpret_cast<u32x4 *>(row + swz<CPT>(2 * c16, t) * 8) = e4m3x8_to_bf16x8_bits(stg[S][i][0], stg[S][i][1]);
+          *reinterpret_cast<u32x4 *>(row + swz<CPT>(2 * c16 + 1, t) * 8) = e4m3x8_to_bf16x8_bits(stg[S][i][2], stg[S][i][3]);
+        }
+        if constexpr (kRopeStage) {
+          if (lane < 32) {
+            const int t = 8 * sw + (lane >> 2), c16 = lane & 3;
+            bf16 *row = buf + C::ROFF + t * DR;
+            *reinterpret_cast<u32x4 *>(row + swz<8>(2 * c16, t) * 8) = e4m3x8_to_bf16x8_bits(stg[S][NPL][0], stg[S][NPL][1]);
+            *reinterpret_cast<u32x4 *>(row + swz<8>(2 * c16 + 1, t) * 8) = e4m3x8_to_bf16x8_bits(stg[S][NPL][2], stg[S][NPL][3]);
+          }
+        }
+      };
+
       // ---- score stage for tile k in buffer ht: S^T for the wave's 16 rows,
       // softmax, hand P over
       auto score_tile = [&](const bf16 *ht, int k) __attribute__((always_inline)) {
@@ -543,26 +604,61 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
         constexpr int I = decltype(idx_tag)::value;
         return I == 0 ? s_b0 : I == 1 ? s_b1 : I == 2 ? s_b2 : s_b3;
       };
-      // prologue: tiles k0 and k0 + 1 (a sequence with no token zero-fills)
-      if (L > 0) {
-        dma_prepare(k0, true);
-        issue_tile(s_b0);
-        dma_prepare(k0 + 1, true);
-        issue_tile(s_b1);
+      // prologue: tiles k0 and k0 + 1 (a sequence with no token zero-fills).
+      // 8-bit cache: tile k0 goes to slot 0 now, tile k0 + 1 waits in
+      // register set 1 (stored at the end of the first iteration).
+      if constexpr (F8) {
+        if (L > 0) {
+          if constexpr (kScore) {
+            dma_prepare(k0, true);
+            stage_load(std::integral_constant<int, 0>{});
+            dma_prepare(k0 + 1, true);
+            stage_load(std::integral_constant<int, 1>{});
+            stage_store(std::integral_constant<int, 0>{}, s_b0);
+          }
+        } else {
+          zero_tile(s_b0);
+#pragma unroll
+          for (int i = 0; i <= NPL; ++i) stg[1][i] = u32x4{0u, 0u, 0u, 0u};
+        }
       } else {
-        zero_tile(s_b0);
-        zero_tile(s_b1);
+        if (L > 0) {
+          dma_prepare(k0, true);
+          issue_tile(s_b0);
+          dma_prepare(k0 + 1, true);
+          issue_tile(s_b1);
+        } else {
+          zero_tile(s_b0);
+          zero_tile(s_b1);
+        }
       }
       if constexpr (kScore) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qreg[ks]));
       }
-      wait_vmem<NI>();  // tile k0 landed (k0 + 1 may be in flight)
+      if constexpr (!F8) wait_vmem<NI>();  // tile k0 landed (k0 + 1 may be in flight)
       tile_barrier();
 
       auto iteration = [&](auto r_tag, int k, auto first_tag) __attribute__((always_inline)) {
         constexpr int R = decltype(r_tag)::value;  // (k - k0) mod 4
         constexpr bool kFirst = decltype(first_tag)::value;
+        if constexpr (F8) {
+          // score waves: tile k + 2 into register set R mod 2 (issued before
+          // the products, so a load has about two iterations to land), tile
+          // k + 1 (set R + 1 mod 2) into ring slot R + 1, whose last tile
+          // (k - 3) was read two iterations ago
+          constexpr int SN = R & 1, SP = SN ^ 1;
+          if constexpr (kScore) {
+            dma_prepare(k + 2, k + 2 < k1 && L > 0);
+            stage_load(std::integral_constant<int, SN>{});
+            if (k < k1) score_tile(buf_of(std::integral_constant<int, R>{}), k);
+            stage_store(std::integral_constant<int, SP>{}, buf_of(std::integral_constant<int, (R + 1) % kRing>{}));
+          } else {
+            if constexpr (!kFirst) value_tile(buf_of(std::integral_constant<int, (R + kRing - 1) % kRing>{}), k - 1);
+          }
+          tile_barrier();
+          return;
+        }
         // The value waves stage their part first and the score waves theirs
         // last: the loads of one role are issued while the other role's
         // products run on the same SIMD (a load stalls its wave while the
@@ -625,7 +721,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
         for (int rb = 0; rb < 4; ++rb) {
           if (rowid[rb] < 0) continue;
           const float v = s_fin[16 * rb + n];
-          const float inv = v > 0.f ? 1.f / v : 0.f;
+          // out_scale: an 8-bit cache's scale (the products ran on codes)
+          const float inv = v > 0.f ? p.out_scale / v : 0.f;
           if (whole) {
             bf16 *out = static_cast<bf16 *>(p.out) + (long long)rowid[rb] * DK + col0;
 #pragma unroll
@@ -657,7 +754,8 @@ template <int DK, int DR>
 hipError_t launch_split(const DecodeParams &p, hipStream_t s, const LaunchEvents &ev) {
   const int G = p.n_kvh * p.row_tiles;
   const int cpad = (p.n_chunks + 7) / 8 * 8;
-  return launch_timed(mla_split_kernel<DK, DR>, dim3(G * cpad), dim3(kThreads), s, ev, p);
+  if (p.fp8) return launch_timed(mla_split_kernel<DK, DR, true>, dim3(G * cpad), dim3(kThreads), s, ev, p);
+  return launch_timed(mla_split_kernel<DK, DR, false>, dim3(G * cpad), dim3(kThreads), s, ev, p);
 }
 
 }  // namespace

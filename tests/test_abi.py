@@ -115,7 +115,7 @@ def _status(lib, a):
     (dict(kv_fp8=1, kv_scale=0.0), 2),
     (dict(kv_fp8=1, kv_scale=float("nan")), 2),
     (dict(kv_fp8=1, kv_scale=0.1, dtype=0), 3),
-    (dict(kv_fp8=1, kv_scale=0.1, d_rope=0), 3),
+    (dict(kv_fp8=1, kv_scale=0.1, h_q=16, d_rope=0), 3),  # few heads, 512 + 0
     (dict(kv_fp8=1, kv_scale=0.1, kv_tok_stride=584, rope_tok_stride=584), 4),
 ])
 def test_mla_validation(lib, change, expect):
