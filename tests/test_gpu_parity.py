@@ -578,6 +578,81 @@ def test_fp8_equals_bf16_of_dequantised_cache(lkv, oracle, kind):
     assert torch.equal(l8, lb)
 
 
+# ------------------------------------------------------------------ limits
+def test_mla_max_query_tokens(lkv, oracle):
+    """s_q = 64, the largest the ABI takes: 1024 query rows on one latent head
+    (16 row tiles on the many-row kernel), one sequence shorter than s_q so
+    that its first rows see nothing under causal masking."""
+    w, x = small_mla(1200, h_q=16, s_q=64, seqlens=(40, 300))
+    note("case mla s_q=64 h_q=16")
+    d = mla_device_inputs(x, w, torch)
+    out, lse = run_mla(lkv, w, d, x=x)
+    ro, rl = oracle_mla(oracle, w, x)
+    assert_close(from_dev(out), ro, from_dev(lse), rl, what="mla s_q=64")
+
+
+def test_gqa_max_query_tokens(lkv, oracle):
+    """s_q = 64 with one query head per KV head: 64 rows per KV head, two
+    32-row tiles, causal masking inside the step."""
+    w, x = _gqa_small(1201, h_q=8, n_kv=8, s_q=64, seqlens=(64, 200, 90))
+    note("case gqa s_q=64 h_q=8 n_kv=8")
+    out, lse = _run_gqa(lkv, w, x)
+    ro, rl = _oracle_gqa(oracle, w, x)
+    assert_close(from_dev(out), ro, from_dev(lse), rl, what="gqa s_q=64")
+
+
+@pytest.mark.parametrize("kind,page", [("mla", 1), ("mla", 1000), ("mla16", 1), ("gqa", 1),
+                                       ("gqa", 1000)])
+def test_extreme_page_sizes(lkv, oracle, kind, page):
+    """One-token pages (every token its own block-table entry) and pages
+    larger than any sequence, not a power of two."""
+    note(f"case page_size={page} {kind}")
+    if kind == "gqa":
+        w, x = _gqa_small(1210 + page, h_q=32, n_kv=8, page=page, seqlens=(100, 333, 65))
+        out, lse = _run_gqa(lkv, w, x)
+        ro, rl = _oracle_gqa(oracle, w, x)
+    else:
+        w, x = small_mla(1220 + page, h_q=128 if kind == "mla" else 16, page=page,
+                         seqlens=(100, 333, 65))
+        out, lse = run_mla(lkv, w, mla_device_inputs(x, w, torch), x=x)
+        ro, rl = oracle_mla(oracle, w, x)
+    assert_close(from_dev(out), ro, from_dev(lse), rl, what=f"{kind} page={page}")
+
+
+@pytest.mark.parametrize("h_q,splits", [(128, 0), (128, 7), (16, 0), (16, 7)])
+def test_many_short_sequences(lkv, oracle, h_q, splits):
+    """300 sequences of 1..40 tokens: many sequences per share, shares that
+    start and end inside a sequence's only tile."""
+    rng = np.random.default_rng(1230 + h_q)
+    seqlens = tuple(int(v) for v in rng.integers(1, 41, size=300))
+    w, x = small_mla(1231 + h_q + splits, h_q=h_q, seqlens=seqlens)
+    note(f"case 300 short sequences h_q={h_q} splits={splits}")
+    out, lse = run_mla(lkv, w, mla_device_inputs(x, w, torch), x=x, num_splits=splits)
+    ro, rl = oracle_mla(oracle, w, x)
+    assert_close(from_dev(out), ro, from_dev(lse), rl, what=f"short h_q={h_q}")
+
+
+@pytest.mark.parametrize("kind", ["gqa", "mla"])
+def test_fp8_scale_not_a_power_of_two(lkv, oracle, kind):
+    """An 8-bit cache whose scale is not a power of two (the folded scales
+    round in float32; the oracle takes kv_scale * code in float64)."""
+    from dataclasses import replace
+    if kind == "gqa":
+        w, _ = _gqa_small(1240, h_q=128, n_kv=8, d_rope=64, s_q=2, cache="fp8")
+    else:
+        w, _ = small_mla(1241, h_q=128, seqlens=(300, 65, 700), cache="fp8")
+    w = replace(w, kv_scale=0.0371)
+    x = li.generate(w)
+    note(f"case fp8 kv_scale=0.0371 {kind}")
+    if kind == "gqa":
+        out, lse = _run_gqa(lkv, w, x, **_fp8(w))
+        ro, rl = _oracle_gqa(oracle, w, dequantised(oracle, x, GQA_KEYS + ["k_rope"], ["q", "q_rope"]))
+    else:
+        out, lse = run_mla(lkv, w, mla_device_inputs(x, w, torch), x=x, **_fp8(w))
+        ro, rl = oracle_mla(oracle, w, dequantised(oracle, x, ["kv"], ["q_nope", "q_rope"]))
+    assert_close(from_dev(out), ro, from_dev(lse), rl, what=f"fp8 scale {kind}")
+
+
 # ------------------------------------------------------- full-size workloads
 FULL = [("dsv3_mla_b64_l4096", 96), ("gla2_b128_l8192", 64), ("ragged_mla_b16_sq1", 48),
         ("ragged_mla_b16_sq2", 48), ("mtp_mla_b64_l4096_sq4", 64), ("gta_b128_l8192", 64)]
