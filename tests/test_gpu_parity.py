@@ -578,6 +578,53 @@ def test_fp8_equals_bf16_of_dequantised_cache(lkv, oracle, kind):
     assert torch.equal(l8, lb)
 
 
+# ----------------------------------------------------- softmax normalisation
+def _pages_of(x, b, page):
+    L = int(x["seqlens"][b])
+    return x["block_table"][b, : (L + page - 1) // page]
+
+
+@pytest.mark.parametrize("kind,h_q,splits", [("mla", 128, 0), ("mla", 128, 7), ("mla", 16, 0),
+                                             ("mla", 16, 5), ("gqa", 32, 0), ("gqa", 32, 7)])
+def test_constant_value_rows_give_that_value(lkv, kind, h_q, splits):
+    """When every cached value row of a sequence is the same vector v, the
+    weights of any row sum to one, so the output is v whatever the scores:
+    a missed rescale of O or of the row sum when the running maximum moves,
+    a wrong share weight in the combine, or a dropped tile would show.
+    Queries are scaled by 8 (exact) so that scores spread and the reference
+    maximum moves.  The row sum adds unrounded probabilities while P V uses
+    their bf16 values, so the check allows one bf16 ulp."""
+    rng = np.random.default_rng(1300 + h_q + splits)
+    seqlens = (300, 1000, 64)
+    if kind == "mla":
+        w, x = small_mla(1301 + h_q + splits, h_q=h_q, seqlens=seqlens)
+        width = w.d_c
+    else:
+        w, x = _gqa_small(1302 + splits, h_q=h_q, n_kv=8, seqlens=seqlens)
+        width = w.d_h
+    v = li.to_bf16_bits(rng.standard_normal((w.B, w.n_kv if kind == "gqa" else 1, width)))
+    for b in range(w.B):
+        pages = _pages_of(x, b, w.page_size)
+        if kind == "mla":
+            x["kv"][pages, :, : w.d_c] = v[b, 0]
+        else:
+            x["v_cache"][pages] = v[b]
+    for k in ("q_nope", "q_rope", "q"):
+        if k in x:
+            x[k] = li.to_bf16_bits(8.0 * li.bf16_bits_to_f32(x[k]))
+    note(f"case constant value rows {kind} h_q={h_q} splits={splits}")
+    if kind == "mla":
+        out, _ = run_mla(lkv, w, mla_device_inputs(x, w, torch), x=x, num_splits=splits)
+    else:
+        out, _ = _run_gqa(lkv, w, x, num_splits=splits)
+    got = from_dev(out)                                   # [B, s_q, h_q, width]
+    hpk = h_q // (w.n_kv if kind == "gqa" else 1)
+    want = li.bf16_bits_to_f32(v)[:, np.arange(h_q) // hpk]  # [B, h_q, width]
+    want = np.broadcast_to(want[:, None], got.shape)
+    assert np.all(np.abs(got - want) <= 2.0 ** -7 * np.abs(want) + 1e-30), \
+        float(np.max(np.abs(got - want) / (np.abs(want) + 1e-30)))
+
+
 # ------------------------------------------------------------------ limits
 def test_mla_max_query_tokens(lkv, oracle):
     """s_q = 64, the largest the ABI takes: 1024 query rows on one latent head
