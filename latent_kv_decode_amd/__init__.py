@@ -99,6 +99,10 @@ class LkvError(RuntimeError):
 _lib = None
 
 
+# LKV_ABI_VERSION of include/lkv.h that the argument structs below follow
+ABI_VERSION = 2
+
+
 def load_library(path: str = LIB_PATH):
     """Load liblkv.so (built by latent_kv_decode_amd.build); raise if absent."""
     global _lib
@@ -109,6 +113,9 @@ def load_library(path: str = LIB_PATH):
         lib = ctypes.CDLL(path)
         lib.lkv_abi_version.restype = ctypes.c_int
         lib.lkv_last_error.restype = ctypes.c_char_p
+        if lib.lkv_abi_version() != ABI_VERSION:
+            raise ImportError(f"{path} has ABI version {lib.lkv_abi_version()}, this binding's "
+                              f"argument structs are version {ABI_VERSION}: rebuild the library")
         for name, argt in [("lkv_mla_decode", MlaArgs), ("lkv_gqa_decode", GqaArgs),
                            ("lkv_gqla_expand_latent", ExpandArgs),
                            ("lkv_split_combine", CombineArgs),

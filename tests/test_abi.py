@@ -250,6 +250,12 @@ def test_proj_and_append_batch_zero_ok(lib):
     assert lib.lkv_append_tokens(ctypes.byref(_append(batch=0))) == 0
 
 
+def test_binding_version_matches_header():
+    hdr = open(os.path.join(ROOT, "include", "lkv.h")).read()
+    m = re.search(r"#define LKV_ABI_VERSION (\d+)", hdr)
+    assert m and int(m.group(1)) == lkv.ABI_VERSION
+
+
 def test_binding_raises_when_library_missing(tmp_path):
     with pytest.raises(ImportError):
         lkv._lib_backup = lkv._lib
