@@ -20,10 +20,11 @@ the split-KV combine).  Other workloads (lkv_inputs.WORKLOADS):
 Timing: W untimed warm-up steps (default 150: the first ~100 steps of a run
 are up to 20% slower while the chip settles), then K timed steps bracketed by
 device synchronisation.  One pair of HIP events on the stream the library launches
-on brackets the K steps (the step time is their span over K), and a pair per
-step, attached by the library to the attention kernel's own launch
-(kernel_events, no marker packets between kernels), times that kernel alone
-for the roofline.  Four
+on brackets the K steps (the step time is their span over K), and a pair on
+every fourth step of the same timed region, attached by the library to the
+attention kernel's own launch (kernel_events, no marker packets between
+kernels), times that kernel alone for the roofline (a pair on every step adds
+about 4 us to each step).  Four
 independent copies of the cache rotate from step to step so that the 256 MB
 Infinity Cache cannot hold the working set.
 
@@ -452,7 +453,8 @@ def main():
     step, work = s["step"], s["work"]
 
     hip = HipEvents()
-    kev = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    ev_every = 4
+    kev = [(hip.create(), hip.create()) for _ in range((args.steps + ev_every - 1) // ev_every)]
     stream = torch.cuda.current_stream()
     log(f"[bench] warmup {args.warmup}")
     for i in range(args.warmup):
@@ -465,7 +467,7 @@ def main():
     t0 = time.perf_counter()
     e_start.record(stream)
     for i in range(args.steps):
-        step(i, kev[i])
+        step(i, kev[i // ev_every] if i % ev_every == 0 else None)
     e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -516,6 +518,8 @@ def main():
         "kernel": f"{s['kernel']} (attention, timed alone); a step adds the split-KV combine "
                   "when a sequence spans several shares",
         "kernel_us": t_kern * 1e6,
+        "kernel_timing": f"HIP events on the attention kernel of every {ev_every}th timed step "
+                         f"({len(kev)} launches)",
         "kernel_us_median_p10_p90": [float(np.median(kern) * 1e6),
                                      float(np.percentile(kern, 10) * 1e6),
                                      float(np.percentile(kern, 90) * 1e6)],
