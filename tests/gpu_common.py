@@ -50,14 +50,21 @@ def assert_close(out, ref, lse=None, lse_ref=None, *, f32=False, what=""):
     ma = float(np.abs(out - ref).max()) if out.size else 0.0
     rl = rel_l2(out, ref) if out.size else 0.0
     lim_ma, lim_rl = (1e-4, 1e-5) if f32 else (OUT_MAX_ABS, OUT_REL_L2)
-    note(f"  {what}: max_abs={ma:.3e} rel_l2={rl:.3e}")
+    # worst per-row relative L2 (rows with a nonzero reference), reported
+    # beside the bound on the whole output
+    rows_o = out.reshape(-1, out.shape[-1]) if out.ndim > 1 else out.reshape(1, -1)
+    rows_r = ref.reshape(rows_o.shape)
+    nr = np.linalg.norm(rows_r, axis=1)
+    live = nr > 0
+    worst = float((np.linalg.norm(rows_o - rows_r, axis=1)[live] / nr[live]).max()) if live.any() else 0.0
+    note(f"  {what}: max_abs={ma:.3e} rel_l2={rl:.3e} worst_row_rel_l2={worst:.3e}")
     assert ma <= lim_ma, f"{what}: max abs error {ma} > {lim_ma}"
     assert rl <= lim_rl, f"{what}: relative L2 error {rl} > {lim_rl}"
     if lse is not None:
         lse = np.asarray(lse, np.float64)
         lse_ref = np.asarray(lse_ref, np.float64)
         both_inf = np.isneginf(lse) & np.isneginf(lse_ref)
-        d = np.abs(np.where(both_inf, 0.0, np.where(both_inf, 0.0, lse) - np.where(both_inf, 0.0, lse_ref)))
+        d = np.abs(np.where(both_inf, 0.0, lse) - np.where(both_inf, 0.0, lse_ref))
         ml = float(d.max()) if d.size else 0.0
         note(f"  {what}: lse max_abs={ml:.3e}")
         assert ml <= (1e-5 if f32 else LSE_MAX_ABS), f"{what}: LSE error {ml}"
