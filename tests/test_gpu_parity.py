@@ -537,7 +537,9 @@ def test_gqa_fp8(lkv, oracle, h_q, n_kv, d_h, d_rope, s_q, splits, page, seqlens
     (128, 1, 512, 2, 5, 48, (70, 600, 129, 2)),
     (32, 2, 256, 1, 0, 64, (0, 300, 1000)),         # GLA-2
     (32, 2, 256, 2, 3, 32, (64, 300, 1000)),
-    (32, 8, 128, 1, 0, 64, (500, 65, 128))])        # GTA
+    (32, 8, 128, 1, 0, 64, (500, 65, 128)),         # GTA
+    (128, 2, 256, 1, 0, 64, (70, 600, 129)),        # GLA-2, many rows per latent head
+    (128, 2, 256, 2, 3, 48, (70, 600, 129))])
 def test_mla_fp8(lkv, oracle, h_q, n_lat, d_c, s_q, splits, page, seqlens):
     w, x = small_mla(950 + h_q + d_c + s_q + page, h_q=h_q, n_lat=n_lat, d_c=d_c, s_q=s_q,
                      page=page, seqlens=seqlens, cache="fp8")
@@ -548,6 +550,21 @@ def test_mla_fp8(lkv, oracle, h_q, n_lat, d_c, s_q, splits, page, seqlens):
     out, lse = run_mla(lkv, w, d, x=x, num_splits=splits, **_fp8(w))
     ro, rl = oracle_mla(oracle, w, dequantised(oracle, x, ["kv"], ["q_nope", "q_rope"]))
     assert_close(from_dev(out), ro, from_dev(lse), rl, what="mla fp8")
+
+
+@pytest.mark.parametrize("d_c,splits", [(512, 0), (256, 5)])
+def test_mla_fp8_many_rows_without_rope(lkv, oracle, d_c, splits):
+    """The many-row kernel's 8-bit instantiations with no RoPE key."""
+    w, x = small_mla(970 + d_c + splits, h_q=128, d_c=d_c, d_rope=0, seqlens=(70, 600, 129),
+                     cache="fp8")
+    note(f"case mla fp8 d_c={d_c} d_rope=0 splits={splits}")
+    d = mla_device_inputs(x, w, torch)
+    out, lse = lkv.lkv_mla_decode(d["q_nope"], None, d["c_kv"], None, d["block_table"],
+                                  d["seqlens"], page_size=w.page_size, softmax_scale=w.scale,
+                                  causal=w.causal, kv_tok_stride=d["kv_tok_stride"],
+                                  num_splits=splits, **_fp8(w))
+    ro, rl = oracle_mla(oracle, w, dequantised(oracle, x, ["kv"], ["q_nope", "q_rope"]))
+    assert_close(from_dev(out), ro, from_dev(lse), rl, what=f"mla fp8 d_c={d_c} no rope")
 
 
 @pytest.mark.parametrize("kind", ["gqa", "gla2", "mla16"])
