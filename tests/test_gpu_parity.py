@@ -595,6 +595,55 @@ def test_fp8_equals_bf16_of_dequantised_cache(lkv, oracle, kind):
     assert torch.equal(l8, lb)
 
 
+# ------------------------------------------------- every compiled instantiation
+# (key width, RoPE width, value width, latent is the value) of the row-tiled
+# kernel, bf16 and 8-bit; each at 16 and at 32 query rows per KV/latent head
+ROW_TILED = [(512, 64, 512, True), (256, 64, 256, True), (128, 64, 128, True),
+             (512, 0, 512, True), (128, 64, 128, False), (128, 0, 128, False),
+             (64, 0, 64, False), (256, 0, 256, False)]
+ROW_TILED_F8 = [(512, 64, 512, True), (256, 64, 256, True), (128, 64, 128, True),
+                (128, 64, 128, False), (128, 0, 128, False)]
+INSTANTIATIONS = ([(v, rows, "") for v in ROW_TILED for rows in (16, 32)]
+                  + [(v, rows, "fp8") for v in ROW_TILED_F8 for rows in (16, 32)]
+                  + [((dk, dr, dk, True), 64, c) for dk in (512, 256) for dr in (64, 0)
+                     for c in ("", "fp8")])
+
+
+@pytest.mark.parametrize("widths,rows,cache", INSTANTIATIONS,
+                         ids=[f"{v[0]}+{v[1]}{'-latent' if v[3] else '-grouped'}-rows{r}{'-' + c if c else ''}"
+                              for v, r, c in INSTANTIATIONS])
+def test_every_instantiation(lkv, oracle, widths, rows, cache):
+    """Each compiled kernel instantiation once, at a small ragged size:
+    latent ones through lkv_mla_decode (one latent head; 64 rows select the
+    many-row kernel), grouped ones through lkv_gqa_decode (two KV heads)."""
+    dk, dr, dv, latent = widths
+    seed = 1400 + dk + dr + rows + (7 if cache else 0) + (3 if latent else 0)
+    note(f"case instantiation {widths} rows={rows} cache={cache or 'bf16'}")
+    q8 = {}
+    if latent:
+        w, x = small_mla(seed, h_q=rows, d_c=dk, d_rope=dr, seqlens=(70, 200, 1), cache=cache)
+        if cache:
+            q8 = _fp8(w)
+        d = mla_device_inputs(x, w, torch)
+        out, lse = lkv.lkv_mla_decode(d["q_nope"], d["q_rope"] if dr else None, d["c_kv"],
+                                      d["k_rope"] if dr else None, d["block_table"], d["seqlens"],
+                                      page_size=w.page_size, softmax_scale=w.scale,
+                                      causal=w.causal, kv_tok_stride=d["kv_tok_stride"],
+                                      rope_tok_stride=d["rope_tok_stride"] if dr else None, **q8)
+        y = dequantised(oracle, x, ["kv"], ["q_nope", "q_rope"]) if cache else x
+        ro, rl = oracle_mla(oracle, w, y)
+    else:
+        w, x = _gqa_small(seed, h_q=2 * rows, n_kv=2, d_h=dk, d_rope=dr, seqlens=(70, 200, 1),
+                          cache=cache)
+        if cache:
+            q8 = _fp8(w)
+        out, lse = _run_gqa(lkv, w, x, **q8)
+        keys = GQA_KEYS + (["k_rope"] if dr else [])
+        y = dequantised(oracle, x, keys, ["q"] + (["q_rope"] if dr else [])) if cache else x
+        ro, rl = _oracle_gqa(oracle, w, y)
+    assert_close(from_dev(out), ro, from_dev(lse), rl, what=f"{widths} rows={rows} {cache}")
+
+
 # ----------------------------------------------------- softmax normalisation
 def _pages_of(x, b, page):
     L = int(x["seqlens"][b])
