@@ -126,11 +126,12 @@ const char *lkv_last_error(void);
  *           the call; queries and output stay bf16.  Each code converts
  *           exactly to bf16, so the arithmetic is that of the bf16 path on
  *           the dequantised values.  Needs dtype LKV_BF16, kv_scale positive
- *           and finite, cache strides multiples of 16 and the widths
- *           (d_c, d_rope) in {(512, 64), (256, 64), (128, 64)}; every row
- *           count (more than 32 rows per latent head run as 32-row tiles
- *           that read the cache through L2).  kv_fp8 = 0: the caches hold
- *           the dtype of the inputs and kv_scale is ignored.
+ *           and finite, cache strides multiples of 16 and 16-byte aligned
+ *           cache pointers, and the widths (d_c, d_rope) in {(512, 64),
+ *           (256, 64), (128, 64)}, plus (512, 0) and (256, 0) when a latent
+ *           head has more than 32 query rows (s_q * h_q / n_latent).
+ *           kv_fp8 = 0: the caches hold the dtype of the inputs and kv_scale
+ *           is ignored.
  *   kernel_events  optional pair of hipEvent_t (either may be NULL), for
  *           timing the attention kernel alone (not the combine pass): they
  *           are attached to that kernel's launch (hipExtLaunchKernel) and

@@ -147,7 +147,8 @@ lkv_status check_shape(const Shape &s) {
     if (!many && !lkv::mfma_decode_supported(s.dk, s.dr, s.dv, s.v_alias, true))
       return fail(LKV_ERR_UNSUPPORTED,
                   "no 8-bit-cache kernel for key width %d + RoPE %d, value width %d (%s); compiled: latent "
-                  "512+64, 256+64, 128+64; grouped 128+64, 128+0",
+                  "512+64, 256+64, 128+64 (and 512+0, 256+0 above 32 rows per latent head); grouped 128+64, "
+                  "128+0",
                   s.dk, s.dr, s.dv, s.v_alias ? "latent" : "grouped");
   } else if (s.dtype == LKV_BF16) {
     const int rows_per_kvh = s.s_q * (s.h_q / s.n_kvh);
