@@ -20,7 +20,9 @@
 // token chunk): 32 products per 32-deep k-step for 12 fragment reads.  The
 // column tiles of one token tile run on one XCD, so that its latent rows are
 // read from HBM once.  float32 accumulation, bf16 output (round to nearest
-// even).
+// even).  The finished tile goes through the (then free) staging LDS in
+// row-major order, so that each token's columns leave as whole 16-byte
+// pieces of contiguous runs rather than as scattered 8-byte stores.
 #include "lkv_internal.h"
 
 namespace lkv {
@@ -62,8 +64,12 @@ __device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
 template <int DH>
 __global__ void __launch_bounds__(kThreadsX) expand_kernel(const ExpandParams p) {
   static_assert(kTN % DH == 0 || DH % kTN == 0, "column tile and group width");
-  __shared__ __attribute__((aligned(16))) bf16 s_c[2][kTM * kKC];
-  __shared__ __attribute__((aligned(16))) bf16 s_w[2][kKC * kTN];
+  // staging buffers (token and weight chunks, double-buffered), reused at
+  // the end for the bf16 output tile [kTM][kTN]
+  static_assert(2 * kTM * kKC + 2 * kKC * kTN == kTM * kTN, "output tile fits the staging LDS");
+  __shared__ __attribute__((aligned(16))) bf16 s_mem[2 * kTM * kKC + 2 * kKC * kTN];
+  bf16(*s_c)[kTM * kKC] = reinterpret_cast<bf16(*)[kTM * kKC]>(s_mem);
+  bf16(*s_w)[kKC * kTN] = reinterpret_cast<bf16(*)[kKC * kTN]>(s_mem + 2 * kTM * kKC);
   __shared__ int s_row[kTM];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, n = lane & 15;
@@ -183,23 +189,38 @@ __global__ void __launch_bounds__(kThreadsX) expand_kernel(const ExpandParams p)
     __syncthreads();
   }
 
-  // ---- D^T tile (columns 4 g .. + 3 of token n per lane) to the caches
+  // ---- D^T tile (columns 4 g .. + 3 of token n per lane) into LDS as a
+  // row-major [token][column] bf16 tile; 16-byte chunk c of token row t at
+  // c ^ 2 (t mod 16), so that the 16 tokens x 4 column groups of one write
+  // hit distinct banks.  (The loop's last barrier ended every read of the
+  // staging buffers.)
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
-    const int row = s_row[128 * wt + 16 * nt + n];
-    if (row < 0) continue;
+    const int tok = 128 * wt + 16 * nt + n;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const int col = col0 + 64 * wc + 16 * mt + 4 * g;
-      if (col >= ncols) continue;
-      const int blk = col / DH, d = col % DH;
-      bf16 *dst = static_cast<bf16 *>(blk < p.g ? p.k_out : p.v_out);
-      const long long ostride = blk < p.g ? p.k_stride : p.v_stride;
+      const int col = 64 * wc + 16 * mt + 4 * g;
+      const int ch = (col >> 3) ^ ((tok & 15) << 1);
       bf16x4 o;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = static_cast<bf16>(acc[mt][nt][i]);
-      *reinterpret_cast<bf16x4 *>(dst + (long long)row * ostride + (long long)(blk % p.g) * DH + d) = o;
+      *reinterpret_cast<bf16x4 *>(s_mem + tok * kTN + ch * 8 + (col & 7)) = o;
     }
+  }
+  __syncthreads();
+  // ---- out: piece q = tid + 512 u is chunk q mod 32 (8 columns) of token
+  // row q / 32; half a wave covers one token's 512 bytes
+#pragma unroll 4
+  for (int u = 0; u < kTM * kTN / 8 / kThreadsX; ++u) {
+    const int q = tid + kThreadsX * u, tok = q >> 5, c = q & 31;
+    const int row = s_row[tok];
+    const int col = col0 + 8 * c;
+    if (row < 0 || col >= ncols) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(s_mem + tok * kTN + ((c ^ ((tok & 15) << 1)) * 8));
+    const int blk = col / DH, d = col % DH;
+    bf16 *dst = static_cast<bf16 *>(blk < p.g ? p.k_out : p.v_out);
+    const long long ostride = blk < p.g ? p.k_stride : p.v_stride;
+    *reinterpret_cast<u32x4 *>(dst + (long long)row * ostride + (long long)(blk % p.g) * DH + d) = v;
   }
 }
 
