@@ -644,6 +644,62 @@ def test_every_instantiation(lkv, oracle, widths, rows, cache):
     assert_close(from_dev(out), ro, from_dev(lse), rl, what=f"{widths} rows={rows} {cache}")
 
 
+# ------------------------------------------------------------ graph capture
+def test_decode_calls_replay_under_a_hip_graph(lkv):
+    """A split MLA call (attention kernel + combine) and a GQA call captured
+    in one graph: every replay, each after eager calls on other inputs and a
+    synchronisation, matches the eager result bit for bit."""
+    w, x = small_mla(1500, h_q=128, seqlens=(300, 1000, 64))
+    d = mla_device_inputs(x, w, torch)
+    wg, xg = _gqa_small(1501, h_q=32, n_kv=8, seqlens=(300, 1000, 64))
+    w2, x2 = small_mla(1502, h_q=128, seqlens=(200, 700, 90))
+    d2 = mla_device_inputs(x2, w2, torch)
+    s = torch.cuda.Stream()
+    ws = torch.empty(lkv.lkv_mla_decode_workspace_size(
+        d["q_nope"], d["q_rope"], d["c_kv"], d["k_rope"], d["block_table"], d["seqlens"],
+        page_size=w.page_size, softmax_scale=w.scale, kv_tok_stride=d["kv_tok_stride"],
+        rope_tok_stride=d["rope_tok_stride"], num_splits=7), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["q_nope"])
+    lse = torch.empty(d["q_nope"].shape[:3], dtype=torch.float32, device="cuda")
+    gq = {k: to_dev(xg[k], torch) for k in ("q", "k_cache", "v_cache")}
+    gbt, gsl = torch.from_numpy(xg["block_table"]).cuda(), torch.from_numpy(xg["seqlens"]).cuda()
+    gout = torch.empty_like(gq["q"])
+    gws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+
+    def step():
+        lkv.lkv_mla_decode(d["q_nope"], d["q_rope"], d["c_kv"], d["k_rope"], d["block_table"],
+                           d["seqlens"], page_size=w.page_size, softmax_scale=w.scale,
+                           kv_tok_stride=d["kv_tok_stride"], rope_tok_stride=d["rope_tok_stride"],
+                           num_splits=7, seqlens_host=x["seqlens"], out=out, lse=lse,
+                           workspace=ws, stream=s)
+        lkv.lkv_gqa_decode(gq["q"], None, gq["k_cache"], gq["v_cache"], None, gbt, gsl,
+                           n_kv=wg.n_kv, page_size=wg.page_size, softmax_scale=wg.scale,
+                           out=gout, workspace=gws, stream=s)
+
+    note("case graph capture: eager reference")
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    ref_o, ref_l, ref_g = out.clone(), lse.clone(), gout.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        # eager work on other inputs between replays
+        run_mla(lkv, w2, d2, x=x2, num_splits=5)
+        out.zero_()
+        lse.zero_()
+        gout.zero_()
+        torch.cuda.synchronize()
+        note(f"case graph capture: replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)), r
+        assert torch.equal(lse, ref_l), r
+        assert torch.equal(gout.view(torch.int16), ref_g.view(torch.int16)), r
+
+
 # ----------------------------------------------------- softmax normalisation
 def _pages_of(x, b, page):
     L = int(x["seqlens"][b])
