@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define LKV_ABI_VERSION 2
+#define LKV_ABI_VERSION 3
 
 typedef enum {
   LKV_OK = 0,
@@ -244,6 +244,14 @@ lkv_status lkv_gqa_decode_workspace_size(const lkv_gqa_args *args, size_t *bytes
  *   start_pos   device int32 [batch] or NULL (= 0): append-only expansion
  *   k_out, v_out  device bf16, element (row, g, e) at row*k_tok_stride + g*d_h + e
  *                 (v_tok_stride for v_out)
+ *   out_fp8, out_scale  8-bit expanded caches: with out_fp8 nonzero, k_out
+ *           and v_out receive OCP 8-bit float E4M3 codes (one byte per
+ *           element, strides in bytes, multiples of 16) of the float32
+ *           results times (1 / out_scale) (the reciprocal taken in float32),
+ *           rounded once to the nearest code (ties to the even code) and
+ *           saturated to +-448 -- the cache that lkv_gqa_decode reads with
+ *           kv_fp8 = 1, kv_scale = out_scale.  out_scale must be positive,
+ *           finite and with a finite float32 reciprocal.
  * Supported: bf16, d_c a multiple of 64 up to 512, d_h in {64, 128, 256}.
  * Rows outside [start_pos, seqlens) are not written.
  * ---------------------------------------------------------------------- */
@@ -263,6 +271,8 @@ typedef struct {
   void *v_out;
   int64_t v_tok_stride;
   void *stream;
+  int32_t out_fp8;  /* nonzero: 8-bit expanded caches, see above */
+  float out_scale;  /* their scale */
 } lkv_expand_args;
 
 lkv_status lkv_gqla_expand_latent(const lkv_expand_args *args);

@@ -69,7 +69,8 @@ class ExpandArgs(ctypes.Structure):
                 ("d_c", _I), ("d_h", _I), ("page_size", _I), ("max_pages", _I), ("c_kv", _V),
                 ("kv_tok_stride", _L), ("w_uk", _V), ("w_uv", _V), ("block_table", _V),
                 ("seqlens", _V), ("start_pos", _V), ("k_out", _V), ("k_tok_stride", _L),
-                ("v_out", _V), ("v_tok_stride", _L), ("stream", _V)]
+                ("v_out", _V), ("v_tok_stride", _L), ("stream", _V), ("out_fp8", _I),
+                ("out_scale", ctypes.c_float)]
 
 
 class CombineArgs(ctypes.Structure):
@@ -100,7 +101,7 @@ _lib = None
 
 
 # LKV_ABI_VERSION of include/lkv.h that the argument structs below follow
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 def load_library(path: str = LIB_PATH):
@@ -354,9 +355,10 @@ def lkv_gqa_decode(q, q_rope, k_cache, v_cache, k_rope, block_table, seqlens, *,
 
 def lkv_gqla_expand_latent(c_kv, w_uk, w_uv, block_table, seqlens, k_out, v_out, *, page_size,
                            kv_tok_stride=None, k_tok_stride=None, v_tok_stride=None,
-                           start_pos=None, stream=None):
+                           start_pos=None, stream=None, out_fp8=False, out_scale=1.0):
     """Expand the latent into g key/value groups (lkv.h: lkv_gqla_expand_latent).
-    w_uk, w_uv [g, d_c, d_h] bf16; k_out / v_out are written in place."""
+    w_uk, w_uv [g, d_c, d_h] bf16; k_out / v_out are written in place (bf16,
+    or with out_fp8 torch.uint8 E4M3 codes of value / out_scale)."""
     g, d_c, d_h = w_uk.shape
     a = ExpandArgs()
     a.struct_size = ctypes.sizeof(ExpandArgs)
@@ -373,6 +375,7 @@ def lkv_gqla_expand_latent(c_kv, w_uk, w_uv, block_table, seqlens, k_out, v_out,
     a.k_tok_stride = g * d_h if k_tok_stride is None else k_tok_stride
     a.v_tok_stride = g * d_h if v_tok_stride is None else v_tok_stride
     a.stream = _stream(stream)
+    a.out_fp8, a.out_scale = int(bool(out_fp8)), float(out_scale)
     _check(load_library().lkv_gqla_expand_latent(ctypes.byref(a)))
     return k_out, v_out
 

@@ -369,6 +369,13 @@ lkv_status lkv_gqla_expand_latent(const lkv_expand_args *a) {
   if (a->kv_tok_stride < a->d_c || a->kv_tok_stride % 8) return fail(LKV_ERR_ALIGN, "kv_tok_stride must be >= d_c and a multiple of 8");
   if (a->k_tok_stride < (long long)a->g * a->d_h || a->v_tok_stride < (long long)a->g * a->d_h || a->k_tok_stride % 4 || a->v_tok_stride % 4)
     return fail(LKV_ERR_SHAPE, "k/v token strides must be >= g * d_h and multiples of 4");
+  if (a->out_fp8) {
+    if (!(a->out_scale > 0.f) || !std::isfinite(a->out_scale) || !std::isfinite(1.f / a->out_scale))
+      return fail(LKV_ERR_SHAPE, "out_scale %g must be positive, finite and have a finite reciprocal",
+                  (double)a->out_scale);
+    if (a->k_tok_stride % 16 || a->v_tok_stride % 16)
+      return fail(LKV_ERR_ALIGN, "8-bit expanded cache token strides must be multiples of 16 bytes");
+  }
   if (a->batch == 0) return LKV_OK;
   if ((long long)a->batch * ((a->max_pages * (long long)a->page_size + 63) / 64) > 0x7fffffffLL)
     return fail(LKV_ERR_SHAPE, "too many tiles for one launch");
@@ -390,6 +397,8 @@ lkv_status lkv_gqla_expand_latent(const lkv_expand_args *a) {
   p.d_h = a->d_h;
   p.page_size = a->page_size;
   p.max_pages = a->max_pages;
+  p.out_fp8 = a->out_fp8 != 0;
+  p.out_inv_scale = a->out_fp8 ? 1.f / a->out_scale : 1.f;
   hipError_t e = lkv::launch_expand(p, static_cast<hipStream_t>(a->stream));
   if (e != hipSuccess) return hip_fail(e, "expansion launch");
   return LKV_OK;

@@ -54,6 +54,22 @@ __device__ __forceinline__ int swz_w(int c, int r) {
   const int t = r & 7;
   return c ^ (((t & 3) << 1) | (t >> 2) | (((r >> 3) & 3) << 3));
 }
+// Nearest OCP E4M3 code of a finite float32 value (ties to the even code;
+// magnitudes past 448 saturate to 448).  Normal results: the mantissa rounded
+// to 3 bits by integer rounding of the float32 bits (a carry moves the
+// exponent); below 2^-6: the nearest multiple of 2^-9, whose code is that
+// multiple (8 lands on 2^-6, code 8).
+__device__ __forceinline__ unsigned e4m3_encode(float x) {
+  const unsigned sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.f);  // NaN -> 448 (fminf); finite inputs only
+  const unsigned b = __float_as_uint(a);
+  // normal: bits rounded at mantissa bit 20; the biased exponent 120 + e
+  // and the 3 mantissa bits then read as code ((e + 7) << 3 | m)
+  const unsigned normal = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - 960u;
+  const unsigned sub = static_cast<unsigned>(rintf(a * 512.f));
+  return (a < 0x1p-6f ? sub : normal) | sign;
+}
+
 __device__ __forceinline__ s16x4 lds_read_tr(const bf16 *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
 }
@@ -187,6 +203,39 @@ __global__ void __launch_bounds__(kThreadsX) expand_kernel(const ExpandParams p)
     // barrier that ended it
     if (kc + 1 < nkc) store_chunk(buf ^ 1);
     __syncthreads();
+  }
+
+  if (p.out_fp8) {
+    // ---- 8-bit caches: codes of value * (1 / out_scale), rounded once from
+    // the float32 results, into LDS as a [token][column] byte tile (16-byte chunk
+    // c of token row t at c ^ (t mod 16)), then out in 16-byte pieces
+    unsigned char *s8 = reinterpret_cast<unsigned char *>(s_mem);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const int tok = 128 * wt + 16 * nt + n;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int col = 64 * wc + 16 * mt + 4 * g;
+        unsigned word = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) word |= e4m3_encode(acc[mt][nt][i] * p.out_inv_scale) << (8 * i);
+        *reinterpret_cast<unsigned *>(s8 + tok * kTN + (((col >> 4) ^ (tok & 15)) << 4) + (col & 15)) = word;
+      }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int u = 0; u < kTM * kTN / 16 / kThreadsX; ++u) {
+      const int q = tid + kThreadsX * u, tok = q >> 4, c = q & 15;
+      const int row = s_row[tok];
+      const int col = col0 + 16 * c;
+      if (row < 0 || col >= ncols) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(s8 + tok * kTN + ((c ^ (tok & 15)) << 4));
+      const int blk = col / DH, d = col % DH;
+      unsigned char *dst = static_cast<unsigned char *>(blk < p.g ? p.k_out : p.v_out);
+      const long long ostride = blk < p.g ? p.k_stride : p.v_stride;
+      *reinterpret_cast<u32x4 *>(dst + (long long)row * ostride + (long long)(blk % p.g) * DH + d) = v;
+    }
+    return;
   }
 
   // ---- D^T tile (columns 4 g .. + 3 of token n per lane) into LDS as a

@@ -93,8 +93,10 @@ struct ExpandParams {
   const void *w_uk, *w_uv;      // [g, d_c, d_h]
   const int32_t *block_table, *seqlens, *start_pos;
   void *k_out, *v_out;
-  long long k_stride, v_stride;
+  long long k_stride, v_stride;  // elements (bf16) or bytes (8-bit output)
   int B, g, d_c, d_h, page_size, max_pages;
+  int out_fp8;                    // nonzero: E4M3 codes of value * out_inv_scale
+  float out_inv_scale;            // 1 / out_scale in float32
 };
 
 // Launchers return hipSuccess or the launch error.  `bf16_variant` selects a

@@ -102,9 +102,11 @@ def gqa_work(seqlens, *, s_q: int, h_q: int, n_kv: int, d_h: int, d_rope: int, p
     return Work(bytes=cache + q + out + meta, flops=flops, cache_bytes=cache)
 
 
-def expand_work(n_tokens: int, *, g: int, d_c: int, d_h: int, elem: int = 2) -> Work:
+def expand_work(n_tokens: int, *, g: int, d_c: int, d_h: int, elem: int = 2,
+                out_elem: int | None = None) -> Work:
     """Latent expansion at cache-write time: read the latent once, write 2g
-    groups of d_h, 2 FLOPs per multiply-add."""
+    groups of d_h (out_elem bytes each: 1 for an 8-bit cache), 2 FLOPs per
+    multiply-add."""
     rd = n_tokens * d_c * elem + 2 * g * d_c * d_h * elem
-    wr = n_tokens * 2 * g * d_h * elem
+    wr = n_tokens * 2 * g * d_h * (elem if out_elem is None else out_elem)
     return Work(bytes=rd + wr, flops=2.0 * n_tokens * d_c * 2 * g * d_h, cache_bytes=rd)

@@ -349,3 +349,19 @@ def e4m3_to_f64(codes, scale=1.0):
     v = np.where(s == 1, -mag, mag)
     v = np.where((e == 15) & (m == 7), np.nan, v)
     return v * scale
+
+
+def e4m3_from_f64(x):
+    """Nearest OCP E4M3 code of each value: ties go to the even code,
+    magnitudes past the largest (448) saturate to it, NaN gives S.1111.111;
+    the sign is bit 7 (so -0.0 gives 0x80).  Searches the magnitudes that
+    e4m3_to_f64 assigns to codes 0x00..0x7E (increasing)."""
+    x = np.asarray(x, dtype=np.float64)
+    mags = e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    a = np.minimum(np.abs(x), mags[-1])
+    hi = np.clip(np.searchsorted(mags, np.nan_to_num(a)), 0, mags.size - 1)
+    lo = np.maximum(hi - 1, 0)
+    below, above = a - mags[lo], mags[hi] - a
+    code = np.where(below < above, lo, np.where(above < below, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = code.astype(np.uint8) | np.where(np.signbit(x), np.uint8(0x80), np.uint8(0))
+    return np.where(np.isnan(x), np.uint8(0x7F) | code & np.uint8(0x80), code).astype(np.uint8)

@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert lkv.lkv_abi_version() == 2
+    assert lkv.lkv_abi_version() == 3
 
 
 def _c_layout(struct, fields):
@@ -176,7 +176,10 @@ def _expand(**kw):
 @pytest.mark.parametrize("change,expect", [
     (dict(dtype=0), 3), (dict(d_c=1024), 3), (dict(d_h=96), 3), (dict(w_uv=None), 1),
     (dict(k_out=FAKE + 8), 4), (dict(kv_tok_stride=500), 4), (dict(k_tok_stride=512), 2),
-    (dict(g=0), 2), (dict(struct_size=3), 7)])
+    (dict(g=0), 2), (dict(struct_size=3), 7),
+    # 8-bit expanded caches
+    (dict(out_fp8=1, out_scale=0.0), 2), (dict(out_fp8=1, out_scale=float("inf")), 2),
+    (dict(out_fp8=1, out_scale=0.1, k_tok_stride=1028), 4)])
 def test_expand_validation(lib, change, expect):
     st = lib.lkv_gqla_expand_latent(ctypes.byref(_expand(**change)))
     assert st == expect, (st, lkv.lkv_last_error())

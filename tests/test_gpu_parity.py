@@ -351,6 +351,120 @@ def test_expand_matches_oracle(lkv, oracle, g, d_c, d_h, seqlens):
         assert np.isnan(got[~valid]).all(), "rows of invalid tokens were written"
 
 
+def _expand_gpu_fp8(lkv, w, x, scale):
+    kv = to_dev(x["kv"], torch)
+    npg = x["num_pages"]
+    k8 = torch.full((npg, w.page_size, w.n_kv, w.d_h), 0x7F, dtype=torch.uint8, device="cuda")
+    v8 = torch.full_like(k8, 0x7F)
+    lkv.lkv_gqla_expand_latent(kv.reshape(-1), to_dev(x["w_uk"], torch), to_dev(x["w_uv"], torch),
+                               torch.from_numpy(x["block_table"]).cuda(),
+                               torch.from_numpy(x["seqlens"]).cuda(), k8, v8,
+                               page_size=w.page_size, kv_tok_stride=w.d_c + w.d_rope,
+                               out_fp8=True, out_scale=scale)
+    return kv, k8, v8
+
+
+@pytest.mark.parametrize("g,d_c,d_h,seqlens", [
+    (8, 512, 128, (130, 64)), (3, 256, 64, (600, 257, 1)), (1, 128, 256, (300, 513))])
+def test_expand_fp8_codes(lkv, oracle, g, d_c, d_h, seqlens):
+    """8-bit expanded caches: the kernel rounds its float32 result once, the
+    oracle its fp64 one, so the codes agree except where a value lies within
+    float32 accumulation error of a midpoint between two codes -- and there
+    the two codes are that midpoint's neighbours."""
+    scale = 1.0 / 16
+    w = li.Workload(name="gqla", kind="gqla", dtype="bf16", B=len(seqlens), h_q=16 * g, s_q=1,
+                    page_size=64, n_lat=1, d_c=d_c, n_kv=g, d_h=d_h, d_rope=64,
+                    seqlens=tuple(seqlens), table="shuffled", scale=1 / math.sqrt(d_h + 64),
+                    seed=720 + g)
+    x = li.generate(w)
+    note(f"case expand fp8 g={g} d_c={d_c} d_h={d_h} seqlens={seqlens}")
+    _, k8, v8 = _expand_gpu_fp8(lkv, w, x, scale)
+    rk, rv = oracle.expand_latent(x["kv"].reshape(-1), _w64(x, "w_uk"), _w64(x, "w_uv"),
+                                  x["block_table"], x["seqlens"], page_size=w.page_size,
+                                  num_pages=x["num_pages"], kv_tok_stride=w.d_c + w.d_rope)
+    valid = li.valid_slot_mask(x["block_table"], x["seqlens"], w.page_size, x["num_pages"])
+    for got8, ref in ((k8, rk), (v8, rv)):
+        got = got8.cpu().numpy()
+        xv = ref[valid] / scale
+        want = oracle.e4m3_from_f64(xv)
+        gv = got[valid]
+        diff = gv != want
+        assert diff.mean() < 1e-2, float(diff.mean())
+        if diff.any():
+            a, b = oracle.e4m3_to_f64(gv[diff]), oracle.e4m3_to_f64(want[diff])
+            mid = (a + b) / 2
+            assert np.all(np.abs(xv[diff] - mid) <= 2e-4 * (np.abs(xv[diff]) + 1)), \
+                float(np.max(np.abs(xv[diff] - mid)))
+        assert (got[~valid] == 0x7F).all(), "rows of invalid tokens were written"
+
+
+def test_expand_fp8_rounding_is_exact(lkv, oracle):
+    """The kernel's E4M3 rounding on exactly known values: W_UK = I and
+    W_UV = -I make K = c and V = -c exactly, so with out_scale 1 the codes
+    must equal the oracle's encoding of c bit for bit -- every code's value,
+    every midpoint between adjacent codes (ties to the even code), points an
+    eighth of a step either side, magnitudes past 448, subnormal ties."""
+    dec, enc = oracle.e4m3_to_f64, oracle.e4m3_from_f64
+    mags = dec(np.arange(0x7F, dtype=np.uint8))
+    mid = (mags[:-1] + mags[1:]) / 2
+    step = mags[1:] - mags[:-1]
+    vals = np.concatenate([mags, mid, mid - step / 8, mid + step / 8,
+                           [448.0, 456.0, 464.0, 472.0, 480.0, 1000.0, 2.0 ** 20,
+                            2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -12, 0.0]])
+    assert np.array_equal(li.bf16_bits_to_f32(li.to_bf16_bits(vals)), vals.astype(np.float32))
+    d = 128
+    w = li.Workload(name="gqla", kind="gqla", dtype="bf16", B=1, h_q=16, s_q=1, page_size=64,
+                    n_lat=1, d_c=d, n_kv=1, d_h=d, d_rope=64, seqlens=(64,), table="shuffled",
+                    scale=1 / math.sqrt(d + 64), seed=1700)
+    x = li.generate(w)
+    cells = np.zeros(64 * d)
+    cells[:vals.size] = vals
+    cells = cells.reshape(64, d)
+    page = x["block_table"][0, 0]
+    x["kv"][page, :, :d] = li.to_bf16_bits(cells)
+    eye = np.eye(d)[None]
+    x["w_uk"], x["w_uv"] = li.to_bf16_bits(eye), li.to_bf16_bits(-eye)
+    note("case expand fp8 exact rounding")
+    _, k8, v8 = _expand_gpu_fp8(lkv, w, x, 1.0)
+    got_k = k8.cpu().numpy()[page, :, 0, :]
+    got_v = v8.cpu().numpy()[page, :, 0, :]
+    assert np.array_equal(got_k, enc(cells)), np.argwhere(got_k != enc(cells))[:5]
+    # V = c (-I) sums products from +0, so an exact zero is +0 (as in the
+    # oracle's fp64 expansion); + 0.0 turns numpy's -0.0 into +0.0
+    want_v = enc(-cells + 0.0)
+    assert np.array_equal(got_v, want_v), np.argwhere(got_v != want_v)[:5]
+
+
+def test_gqla_fp8_expanded_cache_end_to_end(lkv, oracle):
+    """The grouped path over 8-bit caches written by the library: expansion
+    into E4M3 K/V, then grouped decode reading them (with the RoPE key as
+    codes of the same scale), against the oracle's decode over its own
+    expansion quantised by its own encoder."""
+    scale = 1.0 / 16
+    w, x = _gqla_small(1600, seqlens=(130, 64))
+    note("case GQLA over 8-bit expanded caches")
+    _, k8, v8 = _expand_gpu_fp8(lkv, w, x, scale)
+    rope_codes = li.to_e4m3_bits(li.bf16_bits_to_f32(x["kv"][..., w.d_c:]).astype(np.float64) / scale)
+    out, lse = lkv.lkv_gqa_decode(to_dev(x["q_nope_h"], torch), to_dev(x["q_rope"], torch), k8, v8,
+                                  torch.from_numpy(np.ascontiguousarray(rope_codes)).cuda().reshape(-1),
+                                  torch.from_numpy(x["block_table"]).cuda(),
+                                  torch.from_numpy(x["seqlens"]).cuda(), n_kv=w.n_kv,
+                                  page_size=w.page_size, softmax_scale=w.scale,
+                                  rope_tok_stride=w.d_rope, kv_fp8=True, kv_scale=scale)
+    rk, rv = oracle.expand_latent(x["kv"].reshape(-1), _w64(x, "w_uk"), _w64(x, "w_uv"),
+                                  x["block_table"], x["seqlens"], page_size=w.page_size,
+                                  num_pages=x["num_pages"], kv_tok_stride=w.d_c + w.d_rope)
+    kq = oracle.e4m3_to_f64(oracle.e4m3_from_f64(rk / scale), scale)
+    vq = oracle.e4m3_to_f64(oracle.e4m3_from_f64(rv / scale), scale)
+    rq = oracle.e4m3_to_f64(rope_codes, scale)
+    ro, rl = oracle.gqa_decode(_w64(x, "q_nope_h"), np.nan_to_num(kq), np.nan_to_num(vq),
+                               x["block_table"], x["seqlens"], n_kv=w.n_kv, d_h=w.d_h,
+                               page_size=w.page_size, scale=w.scale, causal=w.causal,
+                               q_rope=_w64(x, "q_rope"), k_rope=np.nan_to_num(rq),
+                               d_rope=w.d_rope)
+    assert_close(from_dev(out), ro, from_dev(lse), rl, what="GQLA fp8 expanded")
+
+
 def test_expand_start_pos(lkv):
     w, x = _gqla_small(701)
     sp = np.array([70, 0], np.int32)

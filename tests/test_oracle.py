@@ -463,3 +463,28 @@ def test_e4m3_decode_matches_the_format_definition(oracle_lib):
     assert li.to_e4m3_bits(np.array([1.0625]))[0] == 0x38
     assert li.to_e4m3_bits(np.array([1.1875]))[0] == 0x3A
     assert li.to_e4m3_bits(np.array([1000.0]))[0] == 0x7E
+
+
+def test_e4m3_encode_is_nearest_code(oracle_lib):
+    """The oracle's E4M3 encoding: every finite code round-trips through its
+    value; every midpoint between adjacent codes goes to the even code and
+    points just off it to the nearer one; magnitudes past 448 saturate;
+    signed zero and NaN follow the format."""
+    enc, dec = oracle_lib.e4m3_from_f64, oracle_lib.e4m3_to_f64
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    assert np.array_equal(enc(dec(finite)), finite)
+    pos = np.arange(0x7F, dtype=np.uint8)
+    v = dec(pos)
+    mid = (v[:-1] + v[1:]) / 2
+    even = np.where(pos[:-1] % 2 == 0, pos[:-1], pos[1:])
+    assert np.array_equal(enc(mid), even)
+    step = v[1:] - v[:-1]
+    assert np.array_equal(enc(mid - step / 8), pos[:-1])
+    assert np.array_equal(enc(mid + step / 8), pos[1:])
+    assert np.array_equal(enc(-mid), even | 0x80)
+    assert enc(np.array([448.0]))[0] == 0x7E and enc(np.array([1e6]))[0] == 0x7E
+    assert enc(np.array([-470.0]))[0] == 0xFE
+    assert enc(np.array([-0.0]))[0] == 0x80 and enc(np.array([0.0]))[0] == 0x00
+    assert enc(np.array([2.0 ** -10]))[0] == 0x00            # tie between 0 and 2^-9
+    assert enc(np.array([3 * 2.0 ** -10]))[0] == 0x02        # tie between 2^-9 and 2^-8
+    assert (enc(np.array([np.nan]))[0] & 0x7F) == 0x7F
