@@ -217,7 +217,7 @@ def setup_mla(w, x, args, torch, lkv, rf):
                        d_rope=w.d_rope, page_size=w.page_size, causal=w.causal,
                        cache_elem=1 if fp8 else 2)
     many_rows = w.h_q // w.n_lat * w.s_q > 32 and w.d_c in (256, 512)
-    return dict(step=step, work=work, parity=parity, cpu=cpu,
+    return dict(step=step, work=work, parity=parity, cpu=cpu, out=out,
                 kernel="mla_split_kernel" if many_rows else "mfma_decode_kernel",
                 config={"n_latent": w.n_lat, "d_c": w.d_c, "d_rope": w.d_rope,
                         "cache": "e4m3" if fp8 else "bf16"})
@@ -267,7 +267,7 @@ def setup_gqa(w, x, args, torch, lkv, rf):
 
     work = rf.gqa_work(x["seqlens"], s_q=w.s_q, h_q=w.h_q, n_kv=w.n_kv, d_h=w.d_h, d_rope=0,
                        page_size=w.page_size, causal=w.causal, cache_elem=1 if fp8 else 2)
-    return dict(step=step, work=work, parity=parity, cpu=cpu, kernel="mfma_decode_kernel",
+    return dict(step=step, work=work, parity=parity, cpu=cpu, out=out, kernel="mfma_decode_kernel",
                 config={"n_kv": w.n_kv, "d_h": w.d_h, "d_rope": 0,
                         "cache": "e4m3" if fp8 else "bf16"})
 
@@ -432,7 +432,7 @@ def setup_gqla(w, x, args, torch, lkv, rf):
                             "TFLOP_per_s": proj_flops / t_up / 1e6},
              "append_tokens": {"us": t_app, "bytes": app_bytes, "GB_per_s": app_bytes / t_app / 1e3,
                                "note": "per step, B * s_q new rows of the latent + RoPE cache"}}
-    return dict(step=step, work=work, parity=parity, cpu=cpu, kernel="mfma_decode_kernel",
+    return dict(step=step, work=work, parity=parity, cpu=cpu, out=out, kernel="mfma_decode_kernel",
                 extra=extra, config={"g": w.n_kv, "d_h": w.d_h, "d_rope": w.d_rope, "d_c": w.d_c})
 
 

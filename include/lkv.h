@@ -48,6 +48,18 @@
  *    LSE = -inf.  Device-resident values (lengths, table entries) are a
  *    caller contract: 0 <= L_b <= max_pages * page_size and every table entry
  *    of a used page names a page inside the cache.
+ *  - Host-side checks of that contract.  The entry points that read a block
+ *    table take optional host copies: seqlens_host (int32 [batch]),
+ *    block_table_host (int32 [batch, max_pages]) and num_pages (the number
+ *    of pages in the cache pool, 0 = unknown).  Given seqlens_host, every
+ *    L_b must lie in [0, max_pages * page_size]; given block_table_host too,
+ *    every entry of a used page (the first ceil(L_b / page_size) of row b)
+ *    must be >= 0 and, when num_pages > 0, below num_pages.  A violation
+ *    returns LKV_ERR_SHAPE naming the first bad entry, before any launch.
+ *    The host copies must equal the device values.  With the environment
+ *    variable LKV_DEBUG_CHECKS set to 1 when the library first checks it,
+ *    copies the caller did not give are read back from the device (the
+ *    call then synchronises `stream`) and the same checks run on every call.
  *  - Scores are softmax_scale * <q, k>, with softmax_scale positive and
  *    finite (else LKV_ERR_SHAPE); LSE is the natural log of the sum of
  *    exp(score) over the visible tokens, in float32.
@@ -69,7 +81,7 @@
 extern "C" {
 #endif
 
-#define LKV_ABI_VERSION 3
+#define LKV_ABI_VERSION 4
 
 typedef enum {
   LKV_OK = 0,
@@ -117,8 +129,9 @@ const char *lkv_last_error(void);
  *           group (split-KV; a share may span several sequences and a
  *           sequence several shares; partial results are merged with the
  *           LSE-weighted combine of lkv_split_combine).
- *   seqlens_host  host int32 [batch] copy of seqlens, or NULL.  Used only to
- *           skip the combine pass when no sequence is split; it must then
+ *   seqlens_host  host int32 [batch] copy of seqlens, or NULL.  Used to skip
+ *           the combine pass when no sequence is split, and for the
+ *           host-side checks (with block_table_host, num_pages); it must
  *           equal the device values.
  *   kv_fp8, kv_scale  8-bit cache: with kv_fp8 nonzero, c_kv and k_rope hold
  *           OCP 8-bit float E4M3 codes x8 (one byte per element, strides in
@@ -167,6 +180,9 @@ typedef struct {
   void *kernel_events[2]; /* hipEvent_t or NULL each */
   int32_t kv_fp8;  /* nonzero: 8-bit cache, see above */
   float kv_scale;  /* its dequantisation scale */
+  /* host-side contract checks (see the conventions above); NULL / 0 = none */
+  const int32_t *block_table_host;
+  int64_t num_pages;
 } lkv_mla_args;
 
 lkv_status lkv_mla_decode(const lkv_mla_args *args);
@@ -222,6 +238,8 @@ typedef struct {
   void *kernel_events[2]; /* hipEvent_t or NULL each */
   int32_t kv_fp8;  /* as in lkv_mla_args */
   float kv_scale;
+  const int32_t *block_table_host; /* as in lkv_mla_args */
+  int64_t num_pages;
 } lkv_gqa_args;
 
 lkv_status lkv_gqa_decode(const lkv_gqa_args *args);
@@ -273,6 +291,10 @@ typedef struct {
   void *stream;
   int32_t out_fp8;  /* nonzero: 8-bit expanded caches, see above */
   float out_scale;  /* their scale */
+  /* host-side contract checks (see the conventions above); NULL / 0 = none */
+  const int32_t *seqlens_host;
+  const int32_t *block_table_host;
+  int64_t num_pages;
 } lkv_expand_args;
 
 lkv_status lkv_gqla_expand_latent(const lkv_expand_args *args);
@@ -328,6 +350,10 @@ typedef struct {
   const int32_t *block_table;
   const int32_t *seqlens;
   void *stream;
+  /* host-side contract checks (see the conventions above); NULL / 0 = none */
+  const int32_t *seqlens_host;
+  const int32_t *block_table_host;
+  int64_t num_pages;
 } lkv_append_args;
 
 lkv_status lkv_append_tokens(const lkv_append_args *args);

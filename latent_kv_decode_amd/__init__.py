@@ -49,7 +49,7 @@ class MlaArgs(ctypes.Structure):
                 ("block_table", _V), ("seqlens", _V), ("seqlens_host", _V), ("out", _V),
                 ("lse", _V), ("workspace", _V), ("workspace_bytes", ctypes.c_size_t),
                 ("stream", _V), ("kernel_events", _V * 2), ("kv_fp8", _I),
-                ("kv_scale", ctypes.c_float)]
+                ("kv_scale", ctypes.c_float), ("block_table_host", _V), ("num_pages", _L)]
 
 
 class GqaArgs(ctypes.Structure):
@@ -61,7 +61,8 @@ class GqaArgs(ctypes.Structure):
                 ("rope_tok_stride", _L), ("block_table", _V), ("seqlens", _V),
                 ("seqlens_host", _V), ("out", _V), ("lse", _V), ("workspace", _V),
                 ("workspace_bytes", ctypes.c_size_t), ("stream", _V), ("kernel_events", _V * 2),
-                ("kv_fp8", _I), ("kv_scale", ctypes.c_float)]
+                ("kv_fp8", _I), ("kv_scale", ctypes.c_float), ("block_table_host", _V),
+                ("num_pages", _L)]
 
 
 class ExpandArgs(ctypes.Structure):
@@ -70,7 +71,8 @@ class ExpandArgs(ctypes.Structure):
                 ("kv_tok_stride", _L), ("w_uk", _V), ("w_uv", _V), ("block_table", _V),
                 ("seqlens", _V), ("start_pos", _V), ("k_out", _V), ("k_tok_stride", _L),
                 ("v_out", _V), ("v_tok_stride", _L), ("stream", _V), ("out_fp8", _I),
-                ("out_scale", ctypes.c_float)]
+                ("out_scale", ctypes.c_float), ("seqlens_host", _V), ("block_table_host", _V),
+                ("num_pages", _L)]
 
 
 class CombineArgs(ctypes.Structure):
@@ -88,7 +90,8 @@ class ProjArgs(ctypes.Structure):
 class AppendArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("dtype", _I), ("batch", _I), ("s_q", _I),
                 ("width", _I), ("page_size", _I), ("max_pages", _I), ("src", _V), ("cache", _V),
-                ("tok_stride", _L), ("block_table", _V), ("seqlens", _V), ("stream", _V)]
+                ("tok_stride", _L), ("block_table", _V), ("seqlens", _V), ("stream", _V),
+                ("seqlens_host", _V), ("block_table_host", _V), ("num_pages", _L)]
 
 
 class LkvError(RuntimeError):
@@ -101,7 +104,7 @@ _lib = None
 
 
 # LKV_ABI_VERSION of include/lkv.h that the argument structs below follow
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 def load_library(path: str = LIB_PATH):
@@ -166,15 +169,17 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _stream_obj(stream):
+    return _torch().cuda.current_stream() if stream is None else stream
+
+
 def _stream(stream):
-    torch = _torch()
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(_stream_obj(stream).cuda_stream)
 
 
 def _host_i32(x):
-    """Host int32 array for seqlens_host (kept alive by the caller frame)."""
+    """Host int32 array for seqlens_host / block_table_host (kept alive by the
+    caller frame)."""
     import numpy as np
     if x is None:
         return None, None
@@ -185,16 +190,25 @@ def _host_i32(x):
 _workspaces: dict = {}
 
 
-def _workspace(device, nbytes: int):
-    """Per-device scratch buffer, grown on demand (torch allocation, caller-owned
-    from the library's point of view)."""
+def _workspace(device, stream, nbytes: int):
+    """Scratch buffer for calls that pass no workspace, one per (device,
+    stream), grown on demand.  It is allocated with `stream` current, so
+    torch's caching allocator hands its memory to another tensor only after
+    the work queued on that stream (a buffer replaced when the size grows
+    stays reserved for its stream's pending calls).  Under HIP graph capture
+    the caller must pass the workspace: a graph keeps the pointer, and a
+    cached buffer may be replaced later."""
     torch = _torch()
     if nbytes == 0:
         return None
-    key = str(device)
+    if torch.cuda.is_current_stream_capturing():
+        raise RuntimeError("pass workspace= explicitly when capturing a HIP graph (size from "
+                           "lkv_*_decode_workspace_size); the cached default may be replaced later")
+    key = (str(device), int(stream.cuda_stream))
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(stream):
+            ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -246,7 +260,7 @@ def lkv_mla_decode(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, *, n_late
                    page_size, softmax_scale, causal=True, kv_tok_stride=None,
                    rope_tok_stride=None, num_splits=0, seqlens_host=None, out=None, lse=None,
                    return_lse=True, workspace=None, stream=None, kernel_events=None,
-                   kv_fp8=False, kv_scale=1.0):
+                   kv_fp8=False, kv_scale=1.0, block_table_host=None, num_pages=0):
     """MLA absorbed decode (lkv.h: lkv_mla_decode).  Returns (out, lse).
 
     q_nope [B, s_q, h_q, d_c], q_rope [B, s_q, h_q, d_rope] (or None with
@@ -255,7 +269,9 @@ def lkv_mla_decode(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, *, n_late
     [B, max_pages]; seqlens int32 [B] on the device.  kernel_events: optional
     pair of raw hipEvent_t handles (ints) recorded around the attention kernel.
     kv_fp8 / kv_scale: the caches hold OCP E4M3 codes (torch.uint8) of the
-    values kv_scale * code.
+    values kv_scale * code.  seqlens_host / block_table_host (host int32
+    copies) and num_pages (cache pool size) turn on the library's host-side
+    checks of lengths and table entries before the launch.
     """
     torch = _torch()
     a = _mla_args(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, n_latent, page_size,
@@ -269,17 +285,19 @@ def lkv_mla_decode(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, *, n_late
         lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q_nope.device)
     n = ctypes.c_size_t(0)
     _check(lib.lkv_mla_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)))
+    st = _stream_obj(stream)
     if workspace is None:
-        workspace = _workspace(q_nope.device, n.value)
-    sh, sh_ptr = _host_i32(seqlens_host)
-    a.seqlens_host = sh_ptr
+        workspace = _workspace(q_nope.device, st, n.value)
+    sh, a.seqlens_host = _host_i32(seqlens_host)
+    bh, a.block_table_host = _host_i32(block_table_host)
+    a.num_pages = int(num_pages)
     a.out, a.lse = _ptr(out), _ptr(lse)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    a.stream = _stream(stream)
+    a.stream = ctypes.c_void_p(st.cuda_stream)
     _set_events(a, kernel_events)
     _check(lib.lkv_mla_decode(ctypes.byref(a)))
-    del sh
+    del sh, bh
     return out, lse
 
 
@@ -323,10 +341,10 @@ def lkv_gqa_decode(q, q_rope, k_cache, v_cache, k_rope, block_table, seqlens, *,
                    softmax_scale, causal=True, k_tok_stride=None, v_tok_stride=None,
                    rope_tok_stride=None, num_splits=0, seqlens_host=None, out=None, lse=None,
                    return_lse=True, workspace=None, stream=None, kernel_events=None,
-                   kv_fp8=False, kv_scale=1.0):
+                   kv_fp8=False, kv_scale=1.0, block_table_host=None, num_pages=0):
     """Grouped-query decode over an expanded cache (lkv.h: lkv_gqa_decode).
-    Returns (out [B, s_q, h_q, d_h], lse); kernel_events, kv_fp8 and kv_scale
-    as in lkv_mla_decode."""
+    Returns (out [B, s_q, h_q, d_h], lse); kernel_events, kv_fp8, kv_scale
+    and the host-side checks as in lkv_mla_decode."""
     torch = _torch()
     a = _gqa_args(q, q_rope, k_cache, v_cache, k_rope, block_table, seqlens, n_kv, page_size,
                   softmax_scale, causal, k_tok_stride, v_tok_stride, rope_tok_stride, num_splits,
@@ -339,26 +357,30 @@ def lkv_gqa_decode(q, q_rope, k_cache, v_cache, k_rope, block_table, seqlens, *,
         lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q.device)
     n = ctypes.c_size_t(0)
     _check(lib.lkv_gqa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)))
+    st = _stream_obj(stream)
     if workspace is None:
-        workspace = _workspace(q.device, n.value)
-    sh, sh_ptr = _host_i32(seqlens_host)
-    a.seqlens_host = sh_ptr
+        workspace = _workspace(q.device, st, n.value)
+    sh, a.seqlens_host = _host_i32(seqlens_host)
+    bh, a.block_table_host = _host_i32(block_table_host)
+    a.num_pages = int(num_pages)
     a.out, a.lse = _ptr(out), _ptr(lse)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    a.stream = _stream(stream)
+    a.stream = ctypes.c_void_p(st.cuda_stream)
     _set_events(a, kernel_events)
     _check(lib.lkv_gqa_decode(ctypes.byref(a)))
-    del sh
+    del sh, bh
     return out, lse
 
 
 def lkv_gqla_expand_latent(c_kv, w_uk, w_uv, block_table, seqlens, k_out, v_out, *, page_size,
                            kv_tok_stride=None, k_tok_stride=None, v_tok_stride=None,
-                           start_pos=None, stream=None, out_fp8=False, out_scale=1.0):
+                           start_pos=None, stream=None, out_fp8=False, out_scale=1.0,
+                           seqlens_host=None, block_table_host=None, num_pages=0):
     """Expand the latent into g key/value groups (lkv.h: lkv_gqla_expand_latent).
     w_uk, w_uv [g, d_c, d_h] bf16; k_out / v_out are written in place (bf16,
-    or with out_fp8 torch.uint8 E4M3 codes of value / out_scale)."""
+    or with out_fp8 torch.uint8 E4M3 codes of value / out_scale).  Host-side
+    checks as in lkv_mla_decode."""
     g, d_c, d_h = w_uk.shape
     a = ExpandArgs()
     a.struct_size = ctypes.sizeof(ExpandArgs)
@@ -376,7 +398,11 @@ def lkv_gqla_expand_latent(c_kv, w_uk, w_uv, block_table, seqlens, k_out, v_out,
     a.v_tok_stride = g * d_h if v_tok_stride is None else v_tok_stride
     a.stream = _stream(stream)
     a.out_fp8, a.out_scale = int(bool(out_fp8)), float(out_scale)
+    sh, a.seqlens_host = _host_i32(seqlens_host)
+    bh, a.block_table_host = _host_i32(block_table_host)
+    a.num_pages = int(num_pages)
     _check(load_library().lkv_gqla_expand_latent(ctypes.byref(a)))
+    del sh, bh
     return k_out, v_out
 
 
@@ -433,10 +459,11 @@ def lkv_up_project(o_latent, w_uv, *, out=None, stream=None):
 
 
 def lkv_append_tokens(src, cache, block_table, seqlens, *, page_size, tok_stride=None,
-                      stream=None):
+                      stream=None, seqlens_host=None, block_table_host=None, num_pages=0):
     """Cache write of a step's new tokens (lkv.h: lkv_append_tokens): src
     [B, s_q, width] rows go to positions seqlens[b] - s_q + t of the paged
-    cache (base pointer; row r at r * tok_stride elements)."""
+    cache (base pointer; row r at r * tok_stride elements).  Host-side checks
+    as in lkv_mla_decode."""
     B, s_q, width = src.shape
     a = AppendArgs()
     a.struct_size = ctypes.sizeof(AppendArgs)
@@ -447,5 +474,9 @@ def lkv_append_tokens(src, cache, block_table, seqlens, *, page_size, tok_stride
     a.tok_stride = width if tok_stride is None else tok_stride
     a.block_table, a.seqlens = _ptr(block_table), _ptr(seqlens)
     a.stream = _stream(stream)
+    sh, a.seqlens_host = _host_i32(seqlens_host)
+    bh, a.block_table_host = _host_i32(block_table_host)
+    a.num_pages = int(num_pages)
     _check(load_library().lkv_append_tokens(ctypes.byref(a)))
+    del sh, bh
     return cache

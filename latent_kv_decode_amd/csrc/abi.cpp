@@ -9,8 +9,11 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "lkv.h"
 #include "lkv_internal.h"
@@ -49,6 +52,71 @@ int device_cus(int *out) {
   if (dev >= 0 && dev < 64) cache[dev] = cus;
   *out = cus;
   return 0;
+}
+
+// LKV_DEBUG_CHECKS=1 in the environment (read once): read missing host
+// copies of the lengths and the block table back from the device for the
+// contract checks.
+bool debug_checks() {
+  static const bool on = [] {
+    const char *v = std::getenv("LKV_DEBUG_CHECKS");
+    return v && std::strcmp(v, "1") == 0;
+  }();
+  return on;
+}
+
+// Host copies of the device-resident part of the contract: sequence lengths
+// and block-table entries.  Null members are not checked.
+struct HostView {
+  const int32_t *seqlens;  // [B]
+  const int32_t *table;    // [B, max_pages]
+  long long num_pages;     // pool size, 0 = unknown
+};
+
+// 0 <= L_b <= max_pages * page_size; every entry of a used page names a page
+// of the pool.  Runs on the host before any launch.
+lkv_status check_contract(int B, int page_size, int max_pages, const HostView &h) {
+  if (!h.seqlens || B <= 0) return LKV_OK;
+  const long long cap = (long long)max_pages * page_size;
+  for (int b = 0; b < B; ++b) {
+    const long long L = h.seqlens[b];
+    if (L < 0 || L > cap)
+      return fail(LKV_ERR_SHAPE, "seqlens[%d] = %lld is outside [0, max_pages * page_size = %lld]", b, L, cap);
+    if (!h.table) continue;
+    const long long used = (L + page_size - 1) / page_size;
+    const int32_t *row = h.table + (size_t)b * (size_t)max_pages;
+    for (long long i = 0; i < used; ++i) {
+      const long long pg = row[i];
+      if (pg < 0 || (h.num_pages > 0 && pg >= h.num_pages))
+        return fail(LKV_ERR_SHAPE, "block_table[%d][%lld] = %lld is not a page of the pool (%lld pages)", b, i, pg,
+                    h.num_pages);
+    }
+  }
+  return LKV_OK;
+}
+
+// The contract checks of one call: with the caller's host copies, and under
+// LKV_DEBUG_CHECKS=1 with copies read back from the device for the missing
+// ones (synchronising the stream).
+lkv_status check_call_contract(int B, int page_size, int max_pages, const int32_t *seqlens_dev,
+                               const int32_t *table_dev, HostView h, hipStream_t stream) {
+  std::vector<int32_t> sl, tb;
+  if (debug_checks() && B > 0 && (!h.seqlens || !h.table)) {
+    hipError_t e = hipSuccess;
+    if (!h.seqlens) {
+      sl.resize((size_t)B);
+      e = hipMemcpyAsync(sl.data(), seqlens_dev, sl.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+      h.seqlens = sl.data();
+    }
+    if (e == hipSuccess && !h.table) {
+      tb.resize((size_t)B * (size_t)max_pages);
+      e = hipMemcpyAsync(tb.data(), table_dev, tb.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+      h.table = tb.data();
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "LKV_DEBUG_CHECKS read-back of lengths and block table");
+  }
+  return check_contract(B, page_size, max_pages, h);
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -167,7 +235,8 @@ lkv_status check_shape(const Shape &s) {
 struct Ptrs {
   const void *q, *q_rope, *k, *r, *v;
   long long k_stride, r_stride, v_stride;
-  const int32_t *bt, *seqlens, *seqlens_host;
+  const int32_t *bt, *seqlens, *seqlens_host, *bt_host;
+  long long num_pages;
   void *out;
   float *lse;
   void *ws;
@@ -214,6 +283,9 @@ lkv_status run_decode(const Shape &s, const Ptrs &p, float scale) {
     return fail(LKV_ERR_SHAPE, "softmax_scale %g must be positive and finite", (double)scale);
   if (s.B == 0) return LKV_OK;  // nothing to compute; pointers of empty tensors may be NULL
   if ((st = check_ptrs(s, p)) != LKV_OK) return st;
+  if ((st = check_call_contract(s.B, s.page_size, s.max_pages, p.seqlens, p.bt,
+                                HostView{p.seqlens_host, p.bt_host, p.num_pages}, p.stream)) != LKV_OK)
+    return st;
   Plan pl;
   if ((st = make_plan(s, &pl)) != LKV_OK) return st;
   if (s.dtype == LKV_BF16 && p.ws_bytes < pl.ws_total)
@@ -325,8 +397,9 @@ lkv_status lkv_mla_decode(const lkv_mla_args *a) {
   if (a->n_latent >= 1 && a->kv_tok_stride < (long long)a->n_latent * a->d_c)
     return fail(LKV_ERR_SHAPE, "kv_tok_stride %lld < n_latent * d_c", (long long)a->kv_tok_stride);
   Ptrs p{a->q_nope, a->q_rope, a->c_kv, a->k_rope, a->c_kv, a->kv_tok_stride, a->rope_tok_stride,
-         a->kv_tok_stride, a->block_table, a->seqlens, a->seqlens_host, a->out, a->lse,
-         a->workspace, a->workspace_bytes, static_cast<hipStream_t>(a->stream), a->kernel_events};
+         a->kv_tok_stride, a->block_table, a->seqlens, a->seqlens_host, a->block_table_host,
+         (long long)a->num_pages, a->out, a->lse, a->workspace, a->workspace_bytes,
+         static_cast<hipStream_t>(a->stream), a->kernel_events};
   return run_decode(s, p, a->softmax_scale);
 }
 
@@ -348,8 +421,9 @@ lkv_status lkv_gqa_decode(const lkv_gqa_args *a) {
   const Shape s = gqa_shape(a);
   if (!a->v_cache) return fail(LKV_ERR_NULL, "v_cache is NULL");
   Ptrs p{a->q, a->q_rope, a->k_cache, a->k_rope, a->v_cache, a->k_tok_stride, a->rope_tok_stride,
-         a->v_tok_stride, a->block_table, a->seqlens, a->seqlens_host, a->out, a->lse,
-         a->workspace, a->workspace_bytes, static_cast<hipStream_t>(a->stream), a->kernel_events};
+         a->v_tok_stride, a->block_table, a->seqlens, a->seqlens_host, a->block_table_host,
+         (long long)a->num_pages, a->out, a->lse, a->workspace, a->workspace_bytes,
+         static_cast<hipStream_t>(a->stream), a->kernel_events};
   return run_decode(s, p, a->softmax_scale);
 }
 
@@ -367,8 +441,12 @@ lkv_status lkv_gqla_expand_latent(const lkv_expand_args *a) {
   for (const void *x : all)
     if (!aligned16(x)) return fail(LKV_ERR_ALIGN, "bf16 buffers must be 16-byte aligned");
   if (a->kv_tok_stride < a->d_c || a->kv_tok_stride % 8) return fail(LKV_ERR_ALIGN, "kv_tok_stride must be >= d_c and a multiple of 8");
-  if (a->k_tok_stride < (long long)a->g * a->d_h || a->v_tok_stride < (long long)a->g * a->d_h || a->k_tok_stride % 4 || a->v_tok_stride % 4)
-    return fail(LKV_ERR_SHAPE, "k/v token strides must be >= g * d_h and multiples of 4");
+  if (a->k_tok_stride < (long long)a->g * a->d_h || a->v_tok_stride < (long long)a->g * a->d_h)
+    return fail(LKV_ERR_SHAPE, "k/v token strides must be >= g * d_h");
+  // the output tile leaves in 16-byte pieces: bf16 strides are multiples of
+  // 8 elements
+  if (!a->out_fp8 && (a->k_tok_stride % 8 || a->v_tok_stride % 8))
+    return fail(LKV_ERR_ALIGN, "bf16 expanded cache token strides must be multiples of 8 elements");
   if (a->out_fp8) {
     if (!(a->out_scale > 0.f) || !std::isfinite(a->out_scale) || !std::isfinite(1.f / a->out_scale))
       return fail(LKV_ERR_SHAPE, "out_scale %g must be positive, finite and have a finite reciprocal",
@@ -379,6 +457,12 @@ lkv_status lkv_gqla_expand_latent(const lkv_expand_args *a) {
   if (a->batch == 0) return LKV_OK;
   if ((long long)a->batch * ((a->max_pages * (long long)a->page_size + 63) / 64) > 0x7fffffffLL)
     return fail(LKV_ERR_SHAPE, "too many tiles for one launch");
+  {
+    const lkv_status st = check_call_contract(a->batch, a->page_size, a->max_pages, a->seqlens, a->block_table,
+                                              HostView{a->seqlens_host, a->block_table_host, (long long)a->num_pages},
+                                              static_cast<hipStream_t>(a->stream));
+    if (st != LKV_OK) return st;
+  }
   lkv::ExpandParams p{};
   p.c = a->c_kv;
   p.c_stride = a->kv_tok_stride;
@@ -451,6 +535,12 @@ lkv_status lkv_append_tokens(const lkv_append_args *a) {
   if (!aligned16(a->src) || !aligned16(a->cache)) return fail(LKV_ERR_ALIGN, "src and cache must be 16-byte aligned");
   if ((long long)a->batch * a->s_q > (1LL << 30)) return fail(LKV_ERR_SHAPE, "batch * s_q exceeds 2^30 rows");
   if (a->batch == 0) return LKV_OK;
+  {
+    const lkv_status st = check_call_contract(a->batch, a->page_size, a->max_pages, a->seqlens, a->block_table,
+                                              HostView{a->seqlens_host, a->block_table_host, (long long)a->num_pages},
+                                              static_cast<hipStream_t>(a->stream));
+    if (st != LKV_OK) return st;
+  }
   lkv::AppendParams p{};
   p.src = a->src;
   p.cache = a->cache;

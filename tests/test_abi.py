@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert lkv.lkv_abi_version() == 3
+    assert lkv.lkv_abi_version() == 4
 
 
 def _c_layout(struct, fields):
@@ -267,3 +267,51 @@ def test_binding_raises_when_library_missing(tmp_path):
             lkv.load_library(str(tmp_path / "nope.so"))
         finally:
             lkv._lib = lkv._lib_backup
+
+
+# ------------------------------------------- host-side contract checks
+def _host(arr):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(arr, dtype=np.int32))
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+# max_pages 4, page_size 64: lengths up to 256; a pool of 6 pages
+TABLE_OK = [[3, 0, -1, -1], [5, 1, 2, 4]]
+
+
+@pytest.mark.parametrize("seqlens,table,num_pages,bad", [
+    ([100, 256], TABLE_OK, 6, None),           # padding past the used pages is never read
+    ([100, 256], None, 0, None),               # lengths only
+    ([100, 257], None, 0, "seqlens[1]"),       # longer than max_pages * page_size
+    ([-1, 10], None, 0, "seqlens[0]"),
+    ([129, 10], TABLE_OK, 6, "block_table[0][2]"),   # a used page with id -1
+    ([100, 256], TABLE_OK, 5, "block_table[1][0]"),  # id 5 outside a pool of 5 pages
+    ([100, 256], [[3, 0, -1, -1], [5, 1, -7, 4]], 0, "block_table[1][2]"),
+    ([0, 0], [[-1] * 4, [-1] * 4], 6, None),   # empty sequences use no page
+])
+@pytest.mark.parametrize("entry", ["mla", "gqa", "expand", "append"])
+def test_host_contract_checks(lib, entry, seqlens, table, num_pages, bad):
+    """With host copies of the lengths (and the block table), every length
+    must lie in [0, max_pages * page_size] and every entry of a used page must
+    name a page of the pool; a violation is LKV_ERR_SHAPE before any launch.
+    Inputs that pass go on to the launch (LKV_ERR_HIP without a GPU)."""
+    sl, sl_p = _host(seqlens)
+    bt, bt_p = _host(table) if table is not None else (None, None)
+    a, fn = {"mla": (_mla, lib.lkv_mla_decode), "gqa": (_gqa, lib.lkv_gqa_decode),
+             "expand": (_expand, lib.lkv_gqla_expand_latent),
+             "append": (_append, lib.lkv_append_tokens)}[entry]
+    args = a(seqlens_host=sl_p, block_table_host=bt_p, num_pages=num_pages)
+    st = fn(ctypes.byref(args))
+    if bad is None:
+        assert st in (0, 6), (st, lkv.lkv_last_error())
+    else:
+        assert st == 2, (st, lkv.lkv_last_error())
+        assert bad in lkv.lkv_last_error()
+
+
+def test_expand_bf16_strides_multiple_of_8(lib):
+    """The bf16 expanded cache leaves in 16-byte pieces: strides must be
+    multiples of 8 elements."""
+    assert lib.lkv_gqla_expand_latent(ctypes.byref(_expand(k_tok_stride=1028))) == 4
+    assert lib.lkv_gqla_expand_latent(ctypes.byref(_expand(v_tok_stride=1036))) == 4

@@ -131,18 +131,26 @@ def test_mla_split_share_counts(lkv, oracle):
     assert {1, 2, 3, 4} <= seen and max(seen) > 4, seen
 
 
-@pytest.mark.parametrize("h_q,n_lat,d_c", [(32, 2, 256), (16, 1, 512), (64, 1, 128), (48, 1, 512),
-                                          (32, 8, 128)])
-def test_mla_head_shapes(lkv, oracle, h_q, n_lat, d_c):
+@pytest.mark.parametrize("h_q,n_lat,d_c,s_q,causal", [
+    (32, 2, 256, 1, True), (16, 1, 512, 1, True), (64, 1, 128, 1, True), (48, 1, 512, 1, True),
+    (32, 8, 128, 1, True),
+    # several query tokens with and without causal masking among them on the
+    # row-tiled kernel (at most 32 rows per latent head)
+    (32, 2, 256, 2, False), (16, 1, 512, 2, False), (32, 8, 128, 4, False),
+    (16, 1, 512, 2, True), (32, 8, 128, 4, True)])
+def test_mla_head_shapes(lkv, oracle, h_q, n_lat, d_c, s_q, causal):
     """GLA-2 (two latent heads, shared RoPE key), few heads (one 16-row tile),
     a narrow latent, a head count that leaves a padded row tile, and GTA
-    (eight tied key/value groups of 128 as latent heads, shared RoPE key)."""
-    w, x = small_mla(300 + h_q, B=3, h_q=h_q, n_lat=n_lat, d_c=d_c, seqlens=[77, 300, 129])
-    note(f"case mla_heads h_q={h_q} n_lat={n_lat} d_c={d_c}")
+    (eight tied key/value groups of 128 as latent heads, shared RoPE key);
+    the row-tiled kernel with s_q > 1, causal and not."""
+    w, x = small_mla(300 + h_q + 7 * s_q + (0 if causal else 3), B=3, h_q=h_q, n_lat=n_lat,
+                     d_c=d_c, s_q=s_q, causal=causal, seqlens=[s_q + 76, 300, 129])
+    note(f"case mla_heads h_q={h_q} n_lat={n_lat} d_c={d_c} s_q={s_q} causal={causal}")
     d = mla_device_inputs(x, w, torch)
     out, lse = run_mla(lkv, w, d, x=x)
     ro, rl = oracle_mla(oracle, w, x)
-    assert_close(from_dev(out), ro, from_dev(lse), rl, what=f"mla h_q={h_q} n_lat={n_lat}")
+    assert_close(from_dev(out), ro, from_dev(lse), rl,
+                 what=f"mla h_q={h_q} n_lat={n_lat} s_q={s_q} causal={causal}")
 
 
 @pytest.mark.parametrize("h_q,d_c,d_rope,s_q,splits", [
@@ -285,15 +293,21 @@ def _oracle_gqa(oracle, w, x, rows=None):
                              d_rope=w.d_rope, rows=rows)
 
 
-@pytest.mark.parametrize("h_q,n_kv,d_h,d_rope,s_q,splits", [
-    (32, 8, 128, 0, 1, 0), (128, 8, 128, 64, 2, 0), (128, 8, 128, 64, 2, 7), (64, 2, 64, 0, 1, 3),
-    (16, 16, 256, 0, 1, 0), (8, 1, 128, 0, 2, 0),
+@pytest.mark.parametrize("h_q,n_kv,d_h,d_rope,s_q,splits,causal", [
+    (32, 8, 128, 0, 1, 0, True), (128, 8, 128, 64, 2, 0, True), (128, 8, 128, 64, 2, 7, True),
+    (64, 2, 64, 0, 1, 3, True), (16, 16, 256, 0, 1, 0, True), (8, 1, 128, 0, 2, 0, True),
     # GQLA g = 4, s_q = 1; four query tokens (MTP) on g = 8; GQA-2 with 64
     # query heads per KV head (VHA)
-    (128, 4, 128, 64, 1, 0), (128, 8, 128, 64, 4, 0), (128, 2, 128, 0, 1, 0)])
-def test_gqa_small(lkv, oracle, h_q, n_kv, d_h, d_rope, s_q, splits):
-    w, x = _gqa_small(600 + h_q + d_h, h_q=h_q, n_kv=n_kv, d_h=d_h, d_rope=d_rope, s_q=s_q)
-    note(f"case gqa h_q={h_q} n_kv={n_kv} d_h={d_h} d_rope={d_rope} s_q={s_q} splits={splits}")
+    (128, 4, 128, 64, 1, 0, True), (128, 8, 128, 64, 4, 0, True), (128, 2, 128, 0, 1, 0, True),
+    # no causal masking among the step's query tokens: every token sees the
+    # whole cache, with 16- and 32-row tiles and a split plan
+    (128, 8, 128, 64, 2, 0, False), (128, 8, 128, 64, 2, 5, False), (32, 8, 128, 0, 4, 0, False),
+    (8, 1, 128, 0, 3, 2, False), (64, 2, 64, 0, 4, 0, False)])
+def test_gqa_small(lkv, oracle, h_q, n_kv, d_h, d_rope, s_q, splits, causal):
+    w, x = _gqa_small(600 + h_q + d_h + (0 if causal else 11 * s_q), h_q=h_q, n_kv=n_kv, d_h=d_h,
+                      d_rope=d_rope, s_q=s_q, causal=causal)
+    note(f"case gqa h_q={h_q} n_kv={n_kv} d_h={d_h} d_rope={d_rope} s_q={s_q} splits={splits} "
+         f"causal={causal}")
     out, lse = _run_gqa(lkv, w, x, num_splits=splits)
     ro, rl = _oracle_gqa(oracle, w, x)
     assert_close(from_dev(out), ro, from_dev(lse), rl, what="gqa")
@@ -625,19 +639,23 @@ def _fp8(w):
     return dict(kv_fp8=True, kv_scale=w.kv_scale)
 
 
-@pytest.mark.parametrize("h_q,n_kv,d_h,d_rope,s_q,splits,page,seqlens", [
-    (32, 8, 128, 0, 1, 0, 64, (100, 700, 65)),
-    (128, 8, 128, 64, 2, 0, 64, (100, 700, 65)),     # GQLA grouped, g = 8
-    (128, 8, 128, 64, 2, 7, 64, (100, 700, 65)),
-    (128, 2, 128, 0, 1, 0, 64, (0, 1, 130, 64)),    # GQA-2; empty and 1-token rows
-    (8, 1, 128, 0, 2, 3, 48, (100, 700, 65)),       # general pages
-    (32, 8, 128, 64, 1, 0, 16, (333, 64, 1000))])
-def test_gqa_fp8(lkv, oracle, h_q, n_kv, d_h, d_rope, s_q, splits, page, seqlens):
-    w, x = _gqa_small(900 + h_q + page + splits, h_q=h_q, n_kv=n_kv, d_h=d_h, d_rope=d_rope,
-                      s_q=s_q, page=page, seqlens=seqlens, cache="fp8")
+@pytest.mark.parametrize("h_q,n_kv,d_h,d_rope,s_q,splits,page,seqlens,causal", [
+    (32, 8, 128, 0, 1, 0, 64, (100, 700, 65), True),
+    (128, 8, 128, 64, 2, 0, 64, (100, 700, 65), True),     # GQLA grouped, g = 8
+    (128, 8, 128, 64, 2, 7, 64, (100, 700, 65), True),
+    (128, 2, 128, 0, 1, 0, 64, (0, 1, 130, 64), True),    # GQA-2; empty and 1-token rows
+    (8, 1, 128, 0, 2, 3, 48, (100, 700, 65), True),       # general pages
+    (32, 8, 128, 64, 1, 0, 16, (333, 64, 1000), True),
+    # GQLA grouped with no causal masking among the step's two query tokens
+    (128, 8, 128, 64, 2, 0, 64, (100, 700, 65), False),
+    (128, 8, 128, 64, 2, 3, 48, (2, 700, 129), False)])
+def test_gqa_fp8(lkv, oracle, h_q, n_kv, d_h, d_rope, s_q, splits, page, seqlens, causal):
+    w, x = _gqa_small(900 + h_q + page + splits + (0 if causal else 17), h_q=h_q, n_kv=n_kv,
+                      d_h=d_h, d_rope=d_rope, s_q=s_q, page=page, seqlens=seqlens, cache="fp8",
+                      causal=causal)
     assert x["k_cache"].dtype == np.uint8
     note(f"case gqa fp8 h_q={h_q} n_kv={n_kv} d_rope={d_rope} s_q={s_q} splits={splits} "
-         f"page={page} seqlens={seqlens}")
+         f"page={page} seqlens={seqlens} causal={causal}")
     out, lse = _run_gqa(lkv, w, x, num_splits=splits, **_fp8(w))
     keys = GQA_KEYS + (["k_rope"] if d_rope else [])
     y = dequantised(oracle, x, keys, ["q"] + (["q_rope"] if d_rope else []))
@@ -645,21 +663,25 @@ def test_gqa_fp8(lkv, oracle, h_q, n_kv, d_h, d_rope, s_q, splits, page, seqlens
     assert_close(from_dev(out), ro, from_dev(lse), rl, what="gqa fp8")
 
 
-@pytest.mark.parametrize("h_q,n_lat,d_c,s_q,splits,page,seqlens", [
-    (16, 1, 512, 1, 0, 64, (70, 600, 129, 1)),      # few-head MLA
-    (128, 1, 512, 1, 0, 64, (70, 600, 129, 1)),     # many-row MLA
-    (128, 1, 512, 2, 5, 48, (70, 600, 129, 2)),
-    (32, 2, 256, 1, 0, 64, (0, 300, 1000)),         # GLA-2
-    (32, 2, 256, 2, 3, 32, (64, 300, 1000)),
-    (32, 8, 128, 1, 0, 64, (500, 65, 128)),         # GTA
-    (128, 2, 256, 1, 0, 64, (70, 600, 129)),        # GLA-2, many rows per latent head
-    (128, 2, 256, 2, 3, 48, (70, 600, 129))])
-def test_mla_fp8(lkv, oracle, h_q, n_lat, d_c, s_q, splits, page, seqlens):
-    w, x = small_mla(950 + h_q + d_c + s_q + page, h_q=h_q, n_lat=n_lat, d_c=d_c, s_q=s_q,
-                     page=page, seqlens=seqlens, cache="fp8")
+@pytest.mark.parametrize("h_q,n_lat,d_c,s_q,splits,page,seqlens,causal", [
+    (16, 1, 512, 1, 0, 64, (70, 600, 129, 1), True),      # few-head MLA
+    (128, 1, 512, 1, 0, 64, (70, 600, 129, 1), True),     # many-row MLA
+    (128, 1, 512, 2, 5, 48, (70, 600, 129, 2), True),
+    (32, 2, 256, 1, 0, 64, (0, 300, 1000), True),         # GLA-2
+    (32, 2, 256, 2, 3, 32, (64, 300, 1000), True),
+    (32, 8, 128, 1, 0, 64, (500, 65, 128), True),         # GTA
+    (128, 2, 256, 1, 0, 64, (70, 600, 129), True),        # GLA-2, many rows per latent head
+    (128, 2, 256, 2, 3, 48, (70, 600, 129), True),
+    # no causal masking among the query tokens: GLA-2 on the row-tiled kernel,
+    # and many-row MLA
+    (32, 2, 256, 2, 0, 64, (2, 300, 1000), False),
+    (128, 1, 512, 2, 3, 64, (70, 600, 129), False)])
+def test_mla_fp8(lkv, oracle, h_q, n_lat, d_c, s_q, splits, page, seqlens, causal):
+    w, x = small_mla(950 + h_q + d_c + s_q + page + (0 if causal else 5), h_q=h_q, n_lat=n_lat,
+                     d_c=d_c, s_q=s_q, page=page, seqlens=seqlens, cache="fp8", causal=causal)
     assert x["kv"].dtype == np.uint8
     note(f"case mla fp8 h_q={h_q} n_lat={n_lat} d_c={d_c} s_q={s_q} splits={splits} page={page} "
-         f"seqlens={seqlens}")
+         f"seqlens={seqlens} causal={causal}")
     d = mla_device_inputs(x, w, torch)
     out, lse = run_mla(lkv, w, d, x=x, num_splits=splits, **_fp8(w))
     ro, rl = oracle_mla(oracle, w, dequantised(oracle, x, ["kv"], ["q_nope", "q_rope"]))
@@ -1010,16 +1032,17 @@ def test_full_size_gqla_grouped_sampled(lkv, oracle, name):
                                   page_size=w.page_size, softmax_scale=w.scale,
                                   rope_tok_stride=w.d_c + w.d_rope, seqlens_host=x["seqlens"])
     torch.cuda.synchronize()
-    # oracle grouped path on rows sampled from the first and the last
-    # sequence: fp64 expansion of just those sequences' tokens (their pages
-    # copied into a compact pool), then O3 on the sampled rows
-    seqs = [0, w.B - 1]
+    # oracle grouped path on rows sampled from eight sequences spread over the
+    # batch (first and last included): fp64 expansion of just those
+    # sequences' tokens (their pages copied into a compact pool), then O3 on
+    # the sampled rows
+    seqs = sorted(set(int(v) for v in np.linspace(0, w.B - 1, 8).round()))
     per = w.s_q * w.h_q
     rng = np.random.default_rng(13)
-    rows = np.sort(np.concatenate([s * per + rng.choice(per, 16, replace=False) for s in seqs]))
+    rows = np.sort(np.concatenate([s * per + rng.choice(per, 8, replace=False) for s in seqs]))
     rows = rows.astype(np.int32)
     pages = [x["block_table"][s, : (int(x["seqlens"][s]) + 63) // 64] for s in seqs]
-    sub_bt = np.full((2, x["block_table"].shape[1]), -1, np.int32)
+    sub_bt = np.full((len(seqs), x["block_table"].shape[1]), -1, np.int32)
     pool = []
     for i, pg in enumerate(pages):
         sub_bt[i, : len(pg)] = np.arange(len(pool), len(pool) + len(pg))
