@@ -264,10 +264,14 @@ lkv_status lkv_gqa_decode_workspace_size(const lkv_gqa_args *args, size_t *bytes
  *                 (v_tok_stride for v_out)
  *   out_fp8, out_scale  8-bit expanded caches: with out_fp8 nonzero, k_out
  *           and v_out receive OCP 8-bit float E4M3 codes (one byte per
- *           element, strides in bytes, multiples of 16) of the float32
- *           results times (1 / out_scale) (the reciprocal taken in float32),
- *           rounded once to the nearest code (ties to the even code) and
- *           saturated to +-448 -- the cache that lkv_gqa_decode reads with
+ *           element, strides in bytes, multiples of 16) of y = fl32(r * s),
+ *           where r is the float32 result and s = fl32(1 / out_scale): y is
+ *           rounded to the nearest code (ties to the even code), magnitudes
+ *           past 448 (infinities included) saturate to +-448, and a NaN
+ *           gives the NaN code S.1111.111.  When out_scale is a power of two
+ *           the product is exact and r is rounded once; otherwise the
+ *           float32 product adds one rounding of relative size 2^-24 before
+ *           the encoding.  This is the cache that lkv_gqa_decode reads with
  *           kv_fp8 = 1, kv_scale = out_scale.  out_scale must be positive,
  *           finite and with a finite float32 reciprocal.
  * Supported: bf16, d_c a multiple of 64 up to 512, d_h in {64, 128, 256}.

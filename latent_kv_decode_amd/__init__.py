@@ -24,7 +24,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblkv.so")
+# LKV_LIBRARY names another build of the same library (the tests load a
+# sanitizer build of the host code through it); default: the in-tree build
+LIB_PATH = os.environ.get("LKV_LIBRARY") or os.path.join(_HERE, "liblkv.so")
 
 LKV_OK = 0
 LKV_F32, LKV_BF16 = 0, 1

@@ -25,7 +25,12 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liblkv_oracle.so")
+# LKV_ORACLE_SANITIZE=1: build and load an AddressSanitizer + UBSan build of
+# the oracle instead (for CPU tests run with the sanitizer runtime preloaded)
+SANITIZE = os.environ.get("LKV_ORACLE_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "liblkv_oracle_san.so" if SANITIZE else "liblkv_oracle.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+              "-fno-omit-frame-pointer"]
 
 F32, BF16, F64 = 0, 1, 2
 
@@ -36,7 +41,7 @@ def build(force: bool = True) -> str:
         tmp = _LIB + ".tmp"
         subprocess.check_call(
             ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-             "-o", tmp, _SRC, "-lm"])
+             *(_SAN_FLAGS if SANITIZE else []), "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 

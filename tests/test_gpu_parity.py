@@ -378,20 +378,23 @@ def _expand_gpu_fp8(lkv, w, x, scale):
     return kv, k8, v8
 
 
-@pytest.mark.parametrize("g,d_c,d_h,seqlens", [
-    (8, 512, 128, (130, 64)), (3, 256, 64, (600, 257, 1)), (1, 128, 256, (300, 513))])
-def test_expand_fp8_codes(lkv, oracle, g, d_c, d_h, seqlens):
-    """8-bit expanded caches: the kernel rounds its float32 result once, the
+@pytest.mark.parametrize("g,d_c,d_h,seqlens,scale", [
+    (8, 512, 128, (130, 64), 1.0 / 16), (3, 256, 64, (600, 257, 1), 1.0 / 16),
+    (1, 128, 256, (300, 513), 1.0 / 16),
+    # a scale that is not a power of two: the float32 product with the
+    # float32 reciprocal rounds once more (2^-24 relative) before the encoding
+    (8, 512, 128, (130, 64), 0.37), (3, 256, 64, (600, 257, 1), 0.37)])
+def test_expand_fp8_codes(lkv, oracle, g, d_c, d_h, seqlens, scale):
+    """8-bit expanded caches: the kernel rounds its float32 result, the
     oracle its fp64 one, so the codes agree except where a value lies within
     float32 accumulation error of a midpoint between two codes -- and there
     the two codes are that midpoint's neighbours."""
-    scale = 1.0 / 16
     w = li.Workload(name="gqla", kind="gqla", dtype="bf16", B=len(seqlens), h_q=16 * g, s_q=1,
                     page_size=64, n_lat=1, d_c=d_c, n_kv=g, d_h=d_h, d_rope=64,
                     seqlens=tuple(seqlens), table="shuffled", scale=1 / math.sqrt(d_h + 64),
                     seed=720 + g)
     x = li.generate(w)
-    note(f"case expand fp8 g={g} d_c={d_c} d_h={d_h} seqlens={seqlens}")
+    note(f"case expand fp8 g={g} d_c={d_c} d_h={d_h} seqlens={seqlens} scale={scale}")
     _, k8, v8 = _expand_gpu_fp8(lkv, w, x, scale)
     rk, rv = oracle.expand_latent(x["kv"].reshape(-1), _w64(x, "w_uk"), _w64(x, "w_uv"),
                                   x["block_table"], x["seqlens"], page_size=w.page_size,
@@ -447,6 +450,28 @@ def test_expand_fp8_rounding_is_exact(lkv, oracle):
     # oracle's fp64 expansion); + 0.0 turns numpy's -0.0 into +0.0
     want_v = enc(-cells + 0.0)
     assert np.array_equal(got_v, want_v), np.argwhere(got_v != want_v)[:5]
+
+
+def test_expand_nan_latent_gives_nan(lkv, oracle):
+    """A NaN in a valid token's latent row makes that token's expanded K and V
+    NaN: bf16 NaN on the bf16 path, the E4M3 NaN code (S.1111.111) on the
+    8-bit path -- never a finite (saturated) value."""
+    w, x = _gqla_small(1650, seqlens=(130, 64))
+    b, j = 0, 77
+    page, slot = x["block_table"][b, j // w.page_size], j % w.page_size
+    x["kv"][page, slot, : w.d_c] = li.BF16_NAN
+    note("case expand NaN latent row")
+    _, k_out, v_out = _expand_gpu(lkv, w, x)
+    _, k8, v8 = _expand_gpu_fp8(lkv, w, x, 1.0 / 16)
+    for t in (k_out, v_out):
+        assert np.isnan(from_dev(t)[page, slot]).all()
+    for t in (k8, v8):
+        codes = t.cpu().numpy()
+        assert ((codes[page, slot] & 0x7F) == 0x7F).all()
+        others = np.ones(codes.shape[:2], bool)
+        others[page, slot] = False
+        valid = li.valid_slot_mask(x["block_table"], x["seqlens"], w.page_size, x["num_pages"])
+        assert ((codes[others & valid] & 0x7F) != 0x7F).all()
 
 
 def test_gqla_fp8_expanded_cache_end_to_end(lkv, oracle):
