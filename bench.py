@@ -129,19 +129,28 @@ def f64(bits):
     return li.bf16_bits_to_f32(bits).astype(np.float64)
 
 
-def timed_oracle(run_seqs, B: int, budget_s: float):
+def timed_oracle(run_seqs, B: int, budget_s: float, min_s: float = 1.0):
     """Call run_seqs(s0, n) on growing groups of whole sequences until about
-    budget_s seconds of oracle time or the whole batch; returns
-    (sequences done, seconds)."""
+    budget_s seconds of oracle time or the whole batch; a batch that takes
+    less than min_s is run again from its start until min_s has passed (the
+    tiny workload).  Returns (sequences done, seconds)."""
     done, elapsed, chunk = 0, 0.0, 1
-    while done < B and elapsed < budget_s:
-        n = min(chunk, B - done)
+    while elapsed < budget_s and (done < B or elapsed < min_s):
+        s0 = done % B
+        n = min(chunk, B - s0)
         t0 = time.perf_counter()
-        run_seqs(done, n)
+        run_seqs(s0, n)
         elapsed += time.perf_counter() - t0
         done += n
         chunk = min(chunk * 2, 16)
     return done, elapsed
+
+
+def seq_sample(done: int, B: int) -> str:
+    """Words for the sequences one timed oracle sample covered."""
+    if done <= B:
+        return f"{done} of {B} sequences"
+    return f"{done} sequence evaluations (the batch of {B} run {done / B:.0f} times)"
 
 
 def oracle_inputs(x, w, keys, qkeys):
@@ -176,7 +185,9 @@ def setup_mla(w, x, args, torch, lkv, rf):
     q_nope, q_rope = to_dev(x["q_nope"], torch), to_dev(x["q_rope"], torch)
     bt = torch.from_numpy(x["block_table"]).cuda()
     sl = torch.from_numpy(x["seqlens"]).cuda()
-    out = torch.empty((w.B, w.s_q, w.h_q, w.d_c), dtype=torch.bfloat16, device="cuda")
+    f32 = w.dtype == "f32"
+    out = torch.empty((w.B, w.s_q, w.h_q, w.d_c), dtype=torch.float32 if f32 else torch.bfloat16,
+                      device="cuda")
     lse = torch.empty((w.B, w.s_q, w.h_q), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     fp8 = w.cache == "fp8"
@@ -210,15 +221,15 @@ def setup_mla(w, x, args, torch, lkv, rf):
         done, el = timed_oracle(
             lambda s0, n: oracle_rows(np.arange(s0 * per, (s0 + n) * per, dtype=np.int32)),
             w.B, budget)
-        return done, el, f"{done} of {w.B} sequences (all {w.h_q} heads, {w.s_q} query token(s) " \
+        return done, el, f"{seq_sample(done, w.B)} (all {w.h_q} heads, {w.s_q} query token(s) " \
                          f"each, full cache length) of the timed workload"
 
     work = rf.mla_work(x["seqlens"], s_q=w.s_q, h_q=w.h_q, n_lat=w.n_lat, d_c=w.d_c,
                        d_rope=w.d_rope, page_size=w.page_size, causal=w.causal,
-                       cache_elem=1 if fp8 else 2)
+                       cache_elem=1 if fp8 else (4 if f32 else 2), elem=4 if f32 else 2)
     many_rows = w.h_q // w.n_lat * w.s_q > 32 and w.d_c in (256, 512)
-    return dict(step=step, work=work, parity=parity, cpu=cpu, out=out,
-                kernel="mla_split_kernel" if many_rows else "mfma_decode_kernel",
+    kernel = "f32_decode_kernel" if f32 else "mla_split_kernel" if many_rows else "mfma_decode_kernel"
+    return dict(step=step, work=work, parity=parity, cpu=cpu, out=out, kernel=kernel,
                 config={"n_latent": w.n_lat, "d_c": w.d_c, "d_rope": w.d_rope,
                         "cache": "e4m3" if fp8 else "bf16"})
 
@@ -263,7 +274,7 @@ def setup_gqa(w, x, args, torch, lkv, rf):
         done, el = timed_oracle(
             lambda s0, n: oracle_rows(np.arange(s0 * per, (s0 + n) * per, dtype=np.int32)),
             w.B, budget)
-        return done, el, f"{done} of {w.B} sequences (all {w.h_q} heads) of the timed workload"
+        return done, el, f"{seq_sample(done, w.B)} (all {w.h_q} heads) of the timed workload"
 
     work = rf.gqa_work(x["seqlens"], s_q=w.s_q, h_q=w.h_q, n_kv=w.n_kv, d_h=w.d_h, d_rope=0,
                        page_size=w.page_size, causal=w.causal, cache_elem=1 if fp8 else 2)
@@ -373,7 +384,7 @@ def setup_gqla(w, x, args, torch, lkv, rf):
         done, el = timed_oracle(
             lambda s0, n: oracle_seqs(list(range(s0, s0 + n)), np.arange(n * per, dtype=np.int32)),
             w.B, budget)
-        return done, el, f"{done} of {w.B} sequences: fp64 latent expansion of their tokens " \
+        return done, el, f"{seq_sample(done, w.B)}: fp64 latent expansion of their tokens " \
                          f"plus grouped decode of all {w.h_q} heads x {w.s_q} query tokens"
 
     work = rf.gqa_work(x["seqlens"], s_q=w.s_q, h_q=w.h_q, n_kv=w.n_kv, d_h=w.d_h,
@@ -468,9 +479,7 @@ def main():
 
     lkv.load_library()
     w = li.workload(args.workload)
-    if w.dtype != "bf16":
-        print("bench.py times the bf16 workloads", file=sys.stderr)
-        sys.exit(2)
+    f32 = w.dtype == "f32"
     log(f"[bench] generating {w.name}")
     x = li.generate(w)
     s = SETUPS[w.kind](w, x, args, torch, lkv, rf)
@@ -529,7 +538,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if f32 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "seq_len": int(x["seqlens"].max()),
                    "total_cache_tokens": int(np.sum(x["seqlens"])), "s_q": w.s_q, "h_q": w.h_q,
@@ -537,8 +546,12 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": hbm, "peak": rf.MI355X_HBM_GBPS, "unit": "GB/s",
                      "frac": hbm / rf.MI355X_HBM_GBPS, "traffic": measured_traffic(w.name)},
-        "mfma": {"achieved": tflops, "peak": rf.MI355X_BF16_TFLOPS, "unit": "TFLOP/s",
-                 "frac": tflops / rf.MI355X_BF16_TFLOPS},
+        # the float32 path runs on the vector ALUs (no MFMA): its arithmetic
+        # is placed against the fp32 vector peak instead
+        ("alu" if f32 else "mfma"): {
+            "achieved": tflops, "unit": "TFLOP/s",
+            "peak": rf.MI355X_FP32_TFLOPS if f32 else rf.MI355X_BF16_TFLOPS,
+            "frac": tflops / (rf.MI355X_FP32_TFLOPS if f32 else rf.MI355X_BF16_TFLOPS)},
         "kernel": f"{s['kernel']} (attention, timed alone); a step adds the split-KV combine "
                   "when a sequence spans several shares",
         "kernel_us": t_kern * 1e6,
@@ -555,6 +568,9 @@ def main():
         "parity_sample_rel_l2": rel,
     }
     result.update(s.get("extra", {}))
+    if f32:
+        result["note"] = ("a few kilobytes of cache per step: the kernel is bound by launch "
+                          "latency, far from either roofline")
     if not args.no_cpu_baseline:
         import oracle
         log("[bench] cpu baseline (fp64 oracle)")
@@ -562,6 +578,15 @@ def main():
         result["cpu_baseline"] = {"value": done * w.s_q / el, "unit": "tokens/s",
                                   "cores": oracle.num_threads(), "kind": "oracle",
                                   "sample": f"{sample}; {el:.1f} s"}
+        if f32:
+            # the tiny workload also on one core
+            cores = oracle.num_threads()
+            oracle.set_num_threads(1)
+            done1, el1, sample1 = s["cpu"](args.cpu_budget)
+            oracle.set_num_threads(cores)
+            result["cpu_baseline_single_core"] = {
+                "value": done1 * w.s_q / el1, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"{sample1}; {el1:.1f} s"}
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -159,7 +159,8 @@ lkv_status make_plan(const Shape &s, Plan *pl) {
   pl->latent = kLatentNone;
   if (s.dtype == LKV_BF16 && s.v_alias && rows_per_kvh > 32 && lkv::mla_split_supported(s.dk, s.dr))
     pl->latent = kLatentSplit;
-  pl->rows = pl->latent == kLatentSplit ? lkv::mla_split_rows() : lkv::mfma_decode_rows(rows_per_kvh);
+  pl->rows = pl->latent == kLatentSplit ? lkv::mla_split_rows(s.dk, s.dr, rows_per_kvh, s.fp8)
+                                        : lkv::mfma_decode_rows(rows_per_kvh);
   pl->row_tiles = (rows_per_kvh + pl->rows - 1) / pl->rows;
   int cus = 0;
   if (device_cus(&cus) != 0) return fail(LKV_ERR_HIP, "cannot query the device compute-unit count");
@@ -313,6 +314,7 @@ lkv_status run_decode(const Shape &s, const Ptrs &p, float scale) {
   d.page_shift = log2_exact(s.page_size);
   d.max_pages = s.max_pages;
   d.rows_per_kvh = s.s_q * d.hpk;
+  d.tile_rows = pl.rows;
   d.row_tiles = pl.row_tiles;
   d.n_chunks = pl.n_chunks;
   d.causal = s.causal ? 1 : 0;

@@ -762,7 +762,7 @@ hipError_t launch_split(const DecodeParams &p, hipStream_t s, const LaunchEvents
 
 bool mla_split_supported(int dk, int dr) { return (dk == 512 || dk == 256) && (dr == 64 || dr == 0); }
 
-int mla_split_rows() { return kRows; }
+int mla_split_rows(int, int, int, bool) { return kRows; }
 
 hipError_t launch_mla_split(const DecodeParams &p, hipStream_t s, const LaunchEvents &ev) {
   if (p.dk == 512 && p.dr == 64) return launch_split<512, 64>(p, s, ev);

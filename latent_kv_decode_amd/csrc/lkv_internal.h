@@ -49,6 +49,7 @@ struct DecodeParams {
   int page_size, page_shift;   // page_shift = log2(page_size) or -1
   int max_pages;
   int rows_per_kvh;            // s_q * hpk
+  int tile_rows;               // query rows per work-group (ROWS)
   int row_tiles;               // ceil(rows_per_kvh / ROWS)
   int n_chunks;                // split-KV shares of the concatenated tiles
   int causal;
@@ -112,7 +113,9 @@ hipError_t launch_mfma_decode(const DecodeParams &p, bool v_alias, int rows, hip
 // Latent path with the score and value products on different waves, 64 query
 // rows per work-group (decode_split.hip).
 bool mla_split_supported(int dk, int dr);
-int mla_split_rows();
+// Query rows per work-group of the kernel launch_mla_split uses for these
+// widths, rows per latent head and cache type.
+int mla_split_rows(int dk, int dr, int rows_per_kvh, bool fp8);
 hipError_t launch_mla_split(const DecodeParams &p, hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_f32_decode(const DecodeParams &p, hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_combine(const CombineParams &p, hipStream_t s);

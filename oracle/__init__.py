@@ -134,6 +134,12 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's OpenMP loops for later calls (timing
+    only; the arithmetic and its order per row do not depend on it)."""
+    _load().oracle_set_num_threads(ctypes.c_int(int(n)))
+
+
 def mla_decode(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, *, n_lat, d_c, d_rope,
                page_size, scale, causal=True, kv_tok_stride=None, rope_tok_stride=None,
                range_lo=None, range_hi=None, rows=None):

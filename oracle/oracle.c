@@ -520,3 +520,14 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Thread count for the OpenMP loops of later calls (timing of the oracle on
+ * one core or on all of them; no effect on the arithmetic). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  omp_set_num_threads(n > 0 ? n : 1);
+#else
+  (void)n;
+#endif
+}

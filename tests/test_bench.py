@@ -35,3 +35,31 @@ def test_oracle_copy_of_an_8bit_workload():
     wb = li.workload("gqa_b128_l8192", B=2, seqlens=(70, 130))
     xb = li.generate(wb)
     assert bench.oracle_inputs(xb, wb, ["k_cache"], ["q"]) is xb
+
+
+def test_timed_oracle_repeats_a_small_batch():
+    """A batch that takes less than min_s is run again from its start (the
+    tiny workload); a large batch stops at the budget or at its end."""
+    import bench
+    calls = []
+
+    def run(s0, n):
+        calls.append((s0, n))
+
+    done, el = bench.timed_oracle(run, 2, budget_s=10.0, min_s=0.01)
+    assert done >= 2 and all(0 <= s0 < 2 and s0 + n <= 2 for s0, n in calls)
+    assert "run" in bench.seq_sample(done, 2) or done == 2
+    calls.clear()
+    done, _ = bench.timed_oracle(run, 64, budget_s=10.0, min_s=0.0)
+    assert done == 64 and sum(n for _, n in calls) == 64
+    assert bench.seq_sample(3, 64) == "3 of 64 sequences"
+
+
+def test_oracle_thread_count_can_be_set():
+    import oracle
+    oracle.build(force=False)
+    n = oracle.num_threads()
+    oracle.set_num_threads(1)
+    assert oracle.num_threads() == 1
+    oracle.set_num_threads(n)
+    assert oracle.num_threads() == n
