@@ -192,6 +192,26 @@ lkv_status lkv_mla_decode(const lkv_mla_args *args);
 lkv_status lkv_mla_decode_workspace_size(const lkv_mla_args *args, size_t *bytes);
 
 /* ------------------------------------------------------------------------
+ * lkv_mla_decode_noalloc -- lkv_mla_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the same computation and kernels, with the split
+ * partials and per-sequence plan kept in a static device array of the
+ * library (LKV_NOALLOC_SCRATCH_BYTES per GPU, reserved on each GPU the
+ * library runs on until the process ends) instead of a caller workspace.
+ * args->workspace and args->workspace_bytes are ignored; the caller still
+ * passes every input and output.  Arguments whose workspace size
+ * (lkv_mla_decode_workspace_size) exceeds LKV_NOALLOC_SCRATCH_BYTES are
+ * rejected with LKV_ERR_WORKSPACE before any launch.  No device or host
+ * memory is allocated (LKV_DEBUG_CHECKS read-backs are not done here; the
+ * host-copy checks are).  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (on different streams, or from different
+ * threads) race and must be serialised by the caller.  The array's contents
+ * need no initialisation and are not meaningful after a call.
+ * ---------------------------------------------------------------------- */
+#define LKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+lkv_status lkv_mla_decode_noalloc(const lkv_mla_args *args);
+
+/* ------------------------------------------------------------------------
  * lkv_gqa_decode -- grouped-query decode over an expanded cache [GQLA
  * section 2, GQA path: g groups of K/V width d_h plus the shared RoPE key;
  * with d_rope == 0 it is plain GQA, the X post's "copying"].

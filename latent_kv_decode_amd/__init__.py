@@ -9,6 +9,7 @@ raises: there is no fallback implementation.
 
 Entry points (same names as the C ABI):
   lkv_mla_decode          MLA absorbed decode (and GLA with several latent heads)
+  lkv_mla_decode_noalloc  the same with the library's static scratch (allocates nothing)
   lkv_gqa_decode          grouped-query decode over an expanded cache (GQLA GQA path, plain GQA)
   lkv_gqla_expand_latent  latent -> g key/value groups at cache-write time
   lkv_split_combine       LSE-weighted merge of split-KV partial results
@@ -34,8 +35,9 @@ STATUS_NAMES = {0: "LKV_OK", 1: "LKV_ERR_NULL", 2: "LKV_ERR_SHAPE", 3: "LKV_ERR_
                 4: "LKV_ERR_ALIGN", 5: "LKV_ERR_WORKSPACE", 6: "LKV_ERR_HIP", 7: "LKV_ERR_STRUCT"}
 
 EXPORTED = ["lkv_abi_version", "lkv_last_error", "lkv_mla_decode", "lkv_mla_decode_workspace_size",
-            "lkv_gqa_decode", "lkv_gqa_decode_workspace_size", "lkv_gqla_expand_latent",
-            "lkv_split_combine", "lkv_absorb_query", "lkv_up_project", "lkv_append_tokens"]
+            "lkv_mla_decode_noalloc", "lkv_gqa_decode", "lkv_gqa_decode_workspace_size",
+            "lkv_gqla_expand_latent", "lkv_split_combine", "lkv_absorb_query", "lkv_up_project",
+            "lkv_append_tokens"]
 
 _V = ctypes.c_void_p
 _I = ctypes.c_int32
@@ -122,7 +124,8 @@ def load_library(path: str = LIB_PATH):
         if lib.lkv_abi_version() != ABI_VERSION:
             raise ImportError(f"{path} has ABI version {lib.lkv_abi_version()}, this binding's "
                               f"argument structs are version {ABI_VERSION}: rebuild the library")
-        for name, argt in [("lkv_mla_decode", MlaArgs), ("lkv_gqa_decode", GqaArgs),
+        for name, argt in [("lkv_mla_decode", MlaArgs), ("lkv_mla_decode_noalloc", MlaArgs),
+                           ("lkv_gqa_decode", GqaArgs),
                            ("lkv_gqla_expand_latent", ExpandArgs),
                            ("lkv_split_combine", CombineArgs),
                            ("lkv_absorb_query", ProjArgs), ("lkv_up_project", ProjArgs),
@@ -299,6 +302,35 @@ def lkv_mla_decode(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, *, n_late
     a.stream = ctypes.c_void_p(st.cuda_stream)
     _set_events(a, kernel_events)
     _check(lib.lkv_mla_decode(ctypes.byref(a)))
+    del sh, bh
+    return out, lse
+
+
+def lkv_mla_decode_noalloc(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, *, n_latent=1,
+                           page_size, softmax_scale, causal=True, kv_tok_stride=None,
+                           rope_tok_stride=None, num_splits=0, seqlens_host=None, out=None,
+                           lse=None, return_lse=True, stream=None, kernel_events=None,
+                           kv_fp8=False, kv_scale=1.0, block_table_host=None, num_pages=0):
+    """lkv_mla_decode with the library's static device scratch in place of a
+    workspace (lkv.h: lkv_mla_decode_noalloc): the library allocates nothing.
+    Pass `out` (and `lse`) to keep the binding from allocating them.
+    Returns (out, lse)."""
+    torch = _torch()
+    a = _mla_args(q_nope, q_rope, c_kv, k_rope, block_table, seqlens, n_latent, page_size,
+                  softmax_scale, causal, kv_tok_stride, rope_tok_stride, num_splits, kv_fp8,
+                  kv_scale)
+    B, s_q, h_q, d_c = q_nope.shape
+    if out is None:
+        out = torch.empty((B, s_q, h_q, d_c), dtype=q_nope.dtype, device=q_nope.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q_nope.device)
+    sh, a.seqlens_host = _host_i32(seqlens_host)
+    bh, a.block_table_host = _host_i32(block_table_host)
+    a.num_pages = int(num_pages)
+    a.out, a.lse = _ptr(out), _ptr(lse)
+    a.stream = _stream(stream)
+    _set_events(a, kernel_events)
+    _check(load_library().lkv_mla_decode_noalloc(ctypes.byref(a)))
     del sh, bh
     return out, lse
 

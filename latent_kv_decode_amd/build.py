@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "decode_mfma.hip", "decode_split.hip", "decode_f32.hip", "combine.hip", "expand.hip",
-           "proj.hip"]
+           "proj.hip", "noalloc.hip"]
 
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

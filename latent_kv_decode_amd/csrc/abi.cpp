@@ -277,16 +277,21 @@ lkv_status check_ptrs(const Shape &s, const Ptrs &p) {
   return LKV_OK;
 }
 
-lkv_status run_decode(const Shape &s, const Ptrs &p, float scale) {
+lkv_status run_decode(const Shape &s, const Ptrs &p, float scale, bool readback = true) {
   lkv_status st = check_shape(s);
   if (st != LKV_OK) return st;
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(LKV_ERR_SHAPE, "softmax_scale %g must be positive and finite", (double)scale);
   if (s.B == 0) return LKV_OK;  // nothing to compute; pointers of empty tensors may be NULL
   if ((st = check_ptrs(s, p)) != LKV_OK) return st;
-  if ((st = check_call_contract(s.B, s.page_size, s.max_pages, p.seqlens, p.bt,
-                                HostView{p.seqlens_host, p.bt_host, p.num_pages}, p.stream)) != LKV_OK)
+  if (readback) {
+    if ((st = check_call_contract(s.B, s.page_size, s.max_pages, p.seqlens, p.bt,
+                                  HostView{p.seqlens_host, p.bt_host, p.num_pages}, p.stream)) != LKV_OK)
+      return st;
+  } else if ((st = check_contract(s.B, s.page_size, s.max_pages, HostView{p.seqlens_host, p.bt_host, p.num_pages})) !=
+             LKV_OK) {
     return st;
+  }
   Plan pl;
   if ((st = make_plan(s, &pl)) != LKV_OK) return st;
   if (s.dtype == LKV_BF16 && p.ws_bytes < pl.ws_total)
@@ -403,6 +408,33 @@ lkv_status lkv_mla_decode(const lkv_mla_args *a) {
          (long long)a->num_pages, a->out, a->lse, a->workspace, a->workspace_bytes,
          static_cast<hipStream_t>(a->stream), a->kernel_events};
   return run_decode(s, p, a->softmax_scale);
+}
+
+lkv_status lkv_mla_decode_noalloc(const lkv_mla_args *a) {
+  if (!a) return fail(LKV_ERR_NULL, "args is NULL");
+  if (a->struct_size != sizeof(lkv_mla_args)) return fail(LKV_ERR_STRUCT, "struct_size %u != %zu", a->struct_size, sizeof(lkv_mla_args));
+  const Shape s = mla_shape(a);
+  if (a->n_latent >= 1 && a->kv_tok_stride < (long long)a->n_latent * a->d_c)
+    return fail(LKV_ERR_SHAPE, "kv_tok_stride %lld < n_latent * d_c", (long long)a->kv_tok_stride);
+  lkv_status st = check_shape(s);
+  if (st != LKV_OK) return st;
+  void *ws = nullptr;
+  size_t cap = 0;
+  if (s.B > 0) {
+    Plan pl;
+    if ((st = make_plan(s, &pl)) != LKV_OK) return st;
+    if (pl.ws_total > LKV_NOALLOC_SCRATCH_BYTES)
+      return fail(LKV_ERR_WORKSPACE,
+                  "lkv_mla_decode_noalloc: these arguments need %zu bytes of scratch, above the library's static "
+                  "%zu bytes (LKV_NOALLOC_SCRATCH_BYTES); use lkv_mla_decode with a workspace",
+                  pl.ws_total, (size_t)LKV_NOALLOC_SCRATCH_BYTES);
+    const hipError_t e = lkv::static_scratch(&ws, &cap);
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+  }
+  Ptrs p{a->q_nope, a->q_rope, a->c_kv, a->k_rope, a->c_kv, a->kv_tok_stride, a->rope_tok_stride,
+         a->kv_tok_stride, a->block_table, a->seqlens, a->seqlens_host, a->block_table_host,
+         (long long)a->num_pages, a->out, a->lse, ws, cap, static_cast<hipStream_t>(a->stream), a->kernel_events};
+  return run_decode(s, p, a->softmax_scale, false);
 }
 
 lkv_status lkv_gqa_decode_workspace_size(const lkv_gqa_args *a, size_t *bytes) {

@@ -125,5 +125,8 @@ hipError_t launch_proj(const ProjParams &p, bool up, hipStream_t s);
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
 bool expand_supported(int d_c, int d_h);
 hipError_t launch_expand(const ExpandParams &p, hipStream_t s);
+// Device address and size of the current device's static scratch array
+// (noalloc.hip); the address is looked up once per device.
+hipError_t static_scratch(void **ptr, size_t *bytes);
 
 }  // namespace lkv
