@@ -69,6 +69,7 @@ __global__ void __launch_bounds__(64) f32_decode_kernel(const DecodeParams p) {
   // value column v of token row j in the tile: the latent (MLA) or the
   // staged value part (GQA)
   const int voff = v_alias ? 0 : dq;
+  const int nblk = (p.dv + 63) / 64;  // 64-column blocks of the value
 
   for (int d = lane; d < dq; d += 64) q_l[d] = d < p.dk ? q[d] : qr[d - p.dk];
 
@@ -88,19 +89,20 @@ __global__ void __launch_bounds__(64) f32_decode_kernel(const DecodeParams p) {
     __syncthreads();  // previous tile's reads are done
     // direct-to-LDS loads, all in flight together: element c = 64 i + lane
     // of token row tok goes to tile[tok][c]
-    for (int tok = 0; tok < cnt; ++tok) {
-      const long long r = __shfl(crow, tok);
-      for (int c0 = 0; c0 < width; c0 += 64) {
-        const int c = c0 + lane;
-        if (c < width) {
-          const float *src = c < p.dk ? kc + r * p.k_stride + c
-                             : c < dq ? rc + r * p.r_stride + (c - p.dk)
-                                      : vc + r * p.v_stride + (c - dq);
-          __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(tile + tok * pitch + c0),
-                                           4, 0, 0);
-        }
+    // one region at a time (key, RoPE key, separate value), 64 columns per
+    // instruction
+    auto stage = [&](const float *base, long long stride, int cols, int at) {
+      for (int tok = 0; tok < cnt; ++tok) {
+        const float *src = base + (long long)__builtin_amdgcn_readlane(crow, tok) * stride + lane;
+        float *dst = tile + tok * pitch + at;
+        for (int c0 = 0; c0 < cols; c0 += 64)
+          if (c0 + lane < cols)
+            __builtin_amdgcn_global_load_lds(src + c0, (__attribute__((address_space(3))) void *)(dst + c0), 4, 0, 0);
       }
-    }
+    };
+    stage(kc, p.k_stride, p.dk, 0);
+    if (p.dr) stage(rc, p.r_stride, p.dr, p.dk);
+    if (!v_alias) stage(vc, p.v_stride, p.dv, dq);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     float s = -__builtin_inff();
@@ -118,13 +120,27 @@ __global__ void __launch_bounds__(64) f32_decode_kernel(const DecodeParams p) {
     m = mnew;
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) o[i] *= alpha;
-    for (int jj = 0; jj < cnt; ++jj) {
-      const float pw = __shfl(pj, jj);
-      const float *vr = tile + jj * pitch + voff;
+    // weighted sum: value column lane + 64 i (a wave-uniform bound on i, the
+    // last partial block read clamped and weighted by zero past dv)
+    const float *vt = tile + voff;
 #pragma unroll
-      for (int i = 0; i < kPerLane; ++i) {
+    for (int i = 0; i < kPerLane; ++i) {
+      if (i < nblk) {
         const int d = lane + 64 * i;
-        if (d < p.dv) o[i] += pw * vr[d];
+        const int dc = min(d, p.dv - 1);
+        const float keep = d < p.dv ? 1.f : 0.f;
+        float acc = 0.f;
+        int jj = 0;
+        for (; jj + 4 <= cnt; jj += 4) {
+          const float v0 = vt[(jj + 0) * pitch + dc], v1 = vt[(jj + 1) * pitch + dc];
+          const float v2 = vt[(jj + 2) * pitch + dc], v3 = vt[(jj + 3) * pitch + dc];
+          acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), jj + 0)) * v0;
+          acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), jj + 1)) * v1;
+          acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), jj + 2)) * v2;
+          acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), jj + 3)) * v3;
+        }
+        for (; jj < cnt; ++jj) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), jj)) * vt[jj * pitch + dc];
+        o[i] += keep * acc;
       }
     }
   }
