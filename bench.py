@@ -65,10 +65,11 @@ def source_sha(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the attention kernel from the committed
-    rocprofv3 counter summary of this workload, or None when there is none or
-    the kernel source changed since the counters were taken."""
+def measured_counters(workload: str):
+    """The committed rocprofv3 counter summary of this workload's attention
+    kernel (HBM bytes per launch, matrix-unit busy fraction, shader clock), or
+    None when there is none or the kernel source changed since the counters
+    were taken."""
     path = os.path.join(PROFILES, f"{workload}_counters.json")
     if not os.path.exists(path):
         return None
@@ -76,7 +77,13 @@ def measured_traffic(workload: str):
     src = os.path.join(ROOT, c.get("kernel_source", ""))
     if not os.path.isfile(src) or c.get("kernel_source_sha") != source_sha(src):
         return None
-    return c.get("hbm_bytes_per_launch")
+    return c
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the attention kernel (see measured_counters)."""
+    c = measured_counters(workload)
+    return None if c is None else c.get("hbm_bytes_per_launch")
 
 
 class HipEvents:
@@ -567,6 +574,11 @@ def main():
                         "intensity": work.intensity},
         "parity_sample_rel_l2": rel,
     }
+    c = measured_counters(w.name)
+    if c is not None and "busy" in c:
+        # from the counter run of the same kernel source (rocprofv3 --pmc)
+        result["counters"] = {k: c["busy"][k] for k in
+                              ("mfma_busy_frac", "shader_clock_ghz", "wait_any_frac") if k in c["busy"]}
     result.update(s.get("extra", {}))
     if f32:
         result["note"] = ("a few kilobytes of cache per step: the kernel is bound by launch "

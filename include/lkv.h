@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define LKV_ABI_VERSION 4
+#define LKV_ABI_VERSION 5
 
 typedef enum {
   LKV_OK = 0,
@@ -359,10 +359,19 @@ lkv_status lkv_up_project(const lkv_proj_args *args);
  * + t (skipped when j < 0), i.e. cache row
  * block_table[b][j / page_size]*page_size + j % page_size.
  *   src      device [batch, s_q, width] elements (dtype), dense
- *   cache    device, row r at r*tok_stride elements
+ *   cache    device, row r at r*tok_stride elements (of the cache's type)
  *   seqlens  device int32 [batch]: lengths including the new tokens
- * Supported: bf16 or f32; width*element size and tok_stride*element size
- * multiples of 16 bytes; src and cache 16-byte aligned; tok_stride >= width.
+ *   out_fp8, out_scale  8-bit cache (the caches lkv_mla_decode and
+ *           lkv_gqa_decode read with kv_fp8 = 1, kv_scale = out_scale, e.g.
+ *           the RoPE key beside 8-bit expanded caches): with out_fp8 nonzero
+ *           each bf16 value x becomes the OCP E4M3 code of fl32(x * s), s =
+ *           fl32(1 / out_scale), rounded to the nearest code (ties to even),
+ *           saturating at +-448, NaN to S.1111.111 -- one byte per element.
+ *           Needs dtype LKV_BF16 and out_scale positive, finite, with a
+ *           finite float32 reciprocal.
+ * Supported: bf16 or f32 (8-bit output from bf16); width and tok_stride
+ * multiples of 16 bytes of the cache's element; src and cache 16-byte
+ * aligned; tok_stride >= width.
  * ---------------------------------------------------------------------- */
 typedef struct {
   uint32_t struct_size;
@@ -378,6 +387,8 @@ typedef struct {
   const int32_t *seqlens_host;
   const int32_t *block_table_host;
   int64_t num_pages;
+  int32_t out_fp8;  /* nonzero: 8-bit (E4M3) cache, see above */
+  float out_scale;
 } lkv_append_args;
 
 lkv_status lkv_append_tokens(const lkv_append_args *args);

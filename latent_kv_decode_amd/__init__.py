@@ -95,7 +95,8 @@ class AppendArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("dtype", _I), ("batch", _I), ("s_q", _I),
                 ("width", _I), ("page_size", _I), ("max_pages", _I), ("src", _V), ("cache", _V),
                 ("tok_stride", _L), ("block_table", _V), ("seqlens", _V), ("stream", _V),
-                ("seqlens_host", _V), ("block_table_host", _V), ("num_pages", _L)]
+                ("seqlens_host", _V), ("block_table_host", _V), ("num_pages", _L),
+                ("out_fp8", _I), ("out_scale", ctypes.c_float)]
 
 
 class LkvError(RuntimeError):
@@ -108,7 +109,7 @@ _lib = None
 
 
 # LKV_ABI_VERSION of include/lkv.h that the argument structs below follow
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 def load_library(path: str = LIB_PATH):
@@ -493,12 +494,18 @@ def lkv_up_project(o_latent, w_uv, *, out=None, stream=None):
 
 
 def lkv_append_tokens(src, cache, block_table, seqlens, *, page_size, tok_stride=None,
-                      stream=None, seqlens_host=None, block_table_host=None, num_pages=0):
+                      stream=None, seqlens_host=None, block_table_host=None, num_pages=0,
+                      out_fp8=False, out_scale=1.0):
     """Cache write of a step's new tokens (lkv.h: lkv_append_tokens): src
     [B, s_q, width] rows go to positions seqlens[b] - s_q + t of the paged
-    cache (base pointer; row r at r * tok_stride elements).  Host-side checks
-    as in lkv_mla_decode."""
+    cache (base pointer; row r at r * tok_stride elements).  With out_fp8 the
+    cache (torch.uint8) takes E4M3 codes of the bf16 values / out_scale.
+    Host-side checks as in lkv_mla_decode."""
+    import torch
     B, s_q, width = src.shape
+    want = torch.uint8 if out_fp8 else src.dtype
+    if cache.dtype != want:
+        raise ValueError(f"lkv_append_tokens: cache dtype {cache.dtype}, expected {want}")
     a = AppendArgs()
     a.struct_size = ctypes.sizeof(AppendArgs)
     a.dtype = _dtype_code(src)
@@ -511,6 +518,7 @@ def lkv_append_tokens(src, cache, block_table, seqlens, *, page_size, tok_stride
     sh, a.seqlens_host = _host_i32(seqlens_host)
     bh, a.block_table_host = _host_i32(block_table_host)
     a.num_pages = int(num_pages)
+    a.out_fp8, a.out_scale = int(bool(out_fp8)), float(out_scale)
     _check(load_library().lkv_append_tokens(ctypes.byref(a)))
     del sh, bh
     return cache

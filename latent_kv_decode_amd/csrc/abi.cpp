@@ -561,10 +561,16 @@ lkv_status lkv_append_tokens(const lkv_append_args *a) {
   if (a->batch < 0 || a->s_q < 1 || a->width < 1 || a->page_size < 1 || a->max_pages < 1)
     return fail(LKV_ERR_SHAPE, "non-positive size");
   if ((long long)a->page_size * a->max_pages > (1LL << 30)) return fail(LKV_ERR_SHAPE, "page_size * max_pages exceeds 2^30 tokens");
+  if (a->out_fp8) {
+    if (a->dtype != LKV_BF16) return fail(LKV_ERR_UNSUPPORTED, "an 8-bit cache is written from bf16 rows");
+    if (!(a->out_scale > 0.f) || !std::isfinite(a->out_scale) || !std::isfinite(1.f / a->out_scale))
+      return fail(LKV_ERR_SHAPE, "out_scale %g must be positive, finite and have a finite reciprocal", (double)a->out_scale);
+  }
   const int es = a->dtype == LKV_BF16 ? 2 : 4;
+  const int ces = a->out_fp8 ? 1 : es;  // bytes per cache element
   if (a->tok_stride < a->width) return fail(LKV_ERR_SHAPE, "tok_stride %lld < width %d", (long long)a->tok_stride, a->width);
-  if (((long long)a->width * es) % 16 || (a->tok_stride * es) % 16)
-    return fail(LKV_ERR_ALIGN, "width and tok_stride must be multiples of 16 bytes");
+  if (((long long)a->width * ces) % 16 || (a->tok_stride * ces) % 16)
+    return fail(LKV_ERR_ALIGN, "width and tok_stride must be multiples of 16 bytes of the cache");
   if (!a->src || !a->cache || !a->block_table || !a->seqlens) return fail(LKV_ERR_NULL, "a required pointer is NULL");
   if (!aligned16(a->src) || !aligned16(a->cache)) return fail(LKV_ERR_ALIGN, "src and cache must be 16-byte aligned");
   if ((long long)a->batch * a->s_q > (1LL << 30)) return fail(LKV_ERR_SHAPE, "batch * s_q exceeds 2^30 rows");
@@ -585,7 +591,9 @@ lkv_status lkv_append_tokens(const lkv_append_args *a) {
   p.page_size = a->page_size;
   p.max_pages = a->max_pages;
   p.row_bytes = a->width * es;
-  p.tok_stride_bytes = a->tok_stride * es;
+  p.tok_stride_bytes = a->tok_stride * ces;
+  p.out_fp8 = a->out_fp8 != 0;
+  p.out_inv_scale = a->out_fp8 ? 1.f / a->out_scale : 1.f;
   hipError_t e = lkv::launch_append(p, static_cast<hipStream_t>(a->stream));
   if (e != hipSuccess) return hip_fail(e, "append launch");
   return LKV_OK;

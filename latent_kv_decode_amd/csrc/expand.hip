@@ -23,6 +23,7 @@
 // even).  The finished tile goes through the (then free) staging LDS in
 // row-major order, so that each token's columns leave as whole 16-byte
 // pieces of contiguous runs rather than as scattered 8-byte stores.
+#include "e4m3.h"
 #include "lkv_internal.h"
 
 namespace lkv {
@@ -54,24 +55,6 @@ __device__ __forceinline__ int swz_w(int c, int r) {
   const int t = r & 7;
   return c ^ (((t & 3) << 1) | (t >> 2) | (((r >> 3) & 3) << 3));
 }
-// Nearest OCP E4M3 code of a float32 value (ties to the even code;
-// magnitudes past 448, infinities included, saturate to 448; NaN gives the
-// NaN code S.1111.111 with the value's sign bit).  Normal results: the
-// mantissa rounded to 3 bits by integer rounding of the float32 bits (a carry
-// moves the exponent); below 2^-6: the nearest multiple of 2^-9, whose code is
-// that multiple (8 lands on 2^-6, code 8).
-__device__ __forceinline__ unsigned e4m3_encode(float x) {
-  const unsigned sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fminf(fabsf(x), 448.f);  // NaN -> 448 here; replaced below
-  const unsigned b = __float_as_uint(a);
-  // normal: bits rounded at mantissa bit 20; the biased exponent 120 + e
-  // and the 3 mantissa bits then read as code ((e + 7) << 3 | m)
-  const unsigned normal = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - 960u;
-  const unsigned sub = static_cast<unsigned>(rintf(a * 512.f));
-  const unsigned code = (a < 0x1p-6f ? sub : normal) | sign;
-  return __builtin_isnan(x) ? (0x7Fu | sign) : code;
-}
-
 __device__ __forceinline__ s16x4 lds_read_tr(const bf16 *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
 }

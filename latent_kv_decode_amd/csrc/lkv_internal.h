@@ -84,8 +84,10 @@ struct AppendParams {
   void *cache;                  // cache row r at r * tok_stride_bytes
   const int32_t *block_table, *seqlens;
   int B, s_q, page_size, max_pages;
-  int row_bytes;
+  int row_bytes;                 // of a source row
   long long tok_stride_bytes;
+  int out_fp8;                   // nonzero: bf16 source -> E4M3 codes of value * out_inv_scale
+  float out_inv_scale;
 };
 
 struct ExpandParams {

@@ -17,7 +17,9 @@
 // float32 accumulation, bf16 output.
 //
 // Also the cache write of the new tokens: row t of the step's new rows of
-// sequence b goes to position L_b - s_q + t of its paged cache.
+// sequence b goes to position L_b - s_q + t of its paged cache, as is or as
+// OCP E4M3 codes of the values times 1 / scale (an 8-bit cache).
+#include "e4m3.h"
 #include "lkv_internal.h"
 
 namespace lkv {
@@ -132,6 +134,20 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
   const long long row = (long long)bt[j / p.page_size] * p.page_size + j % p.page_size;
   const char *src = static_cast<const char *>(p.src) + r * p.row_bytes;
   char *dst = static_cast<char *>(p.cache) + row * p.tok_stride_bytes;
+  if (p.out_fp8) {
+    // eight bf16 values (16 bytes of the source row) -> eight codes
+    for (int o = 16 * lane; o < p.row_bytes; o += 16 * 64) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(src + o);
+      unsigned w[2] = {0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const unsigned half = (v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        w[i >> 2] |= e4m3_encode(__uint_as_float(half << 16) * p.out_inv_scale) << (8 * (i & 3));
+      }
+      *reinterpret_cast<unsigned long long *>(dst + o / 2) = ((unsigned long long)w[1] << 32) | w[0];
+    }
+    return;
+  }
   for (int o = 16 * lane; o < p.row_bytes; o += 16 * 64)
     *reinterpret_cast<u32x4 *>(dst + o) = *reinterpret_cast<const u32x4 *>(src + o);
 }

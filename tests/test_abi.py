@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert lkv.lkv_abi_version() == 4
+    assert lkv.lkv_abi_version() == 5
 
 
 def _c_layout(struct, fields):
@@ -241,7 +241,14 @@ def _append(**kw):
 @pytest.mark.parametrize("change,expect", [
     (dict(struct_size=8), 7), (dict(dtype=4), 3), (dict(width=0), 2), (dict(width=580, tok_stride=1168), 4),
     (dict(tok_stride=500), 2), (dict(tok_stride=580), 4), (dict(cache=FAKE + 2), 4),
-    (dict(seqlens=None), 1), (dict(page_size=0), 2)])
+    (dict(seqlens=None), 1), (dict(page_size=0), 2),
+    # 8-bit cache: bf16 source only, a usable scale, 16-byte rows of codes
+    (dict(out_fp8=1, out_scale=1.0, dtype=lkv.LKV_F32), 3), (dict(out_fp8=1, out_scale=0.0), 2),
+    (dict(out_fp8=1, out_scale=-1.0), 2), (dict(out_fp8=1, out_scale=float("nan")), 2),
+    (dict(out_fp8=1, out_scale=float("inf")), 2), (dict(out_fp8=1, out_scale=1e-39), 2),
+    (dict(out_fp8=1, out_scale=1.0, width=584, tok_stride=584), 4),
+    (dict(out_fp8=1, out_scale=1.0, tok_stride=580), 4),
+    (dict(out_fp8=1, out_scale=1.0, width=32, tok_stride=48, batch=0), 0)])
 def test_append_validation(lib, change, expect):
     st = lib.lkv_append_tokens(ctypes.byref(_append(**change)))
     assert st == expect, (st, lkv.lkv_last_error())

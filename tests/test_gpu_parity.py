@@ -476,19 +476,33 @@ def test_expand_nan_latent_gives_nan(lkv, oracle):
 
 def test_gqla_fp8_expanded_cache_end_to_end(lkv, oracle):
     """The grouped path over 8-bit caches written by the library: expansion
-    into E4M3 K/V, then grouped decode reading them (with the RoPE key as
-    codes of the same scale), against the oracle's decode over its own
-    expansion quantised by its own encoder."""
+    into E4M3 K/V and the RoPE key appended as codes of the same scale (every
+    position of each sequence in one append of s_q = the longest length),
+    then grouped decode reading them, against the oracle's decode over its
+    own expansion quantised by its own encoder."""
     scale = 1.0 / 16
     w, x = _gqla_small(1600, seqlens=(130, 64))
     note("case GQLA over 8-bit expanded caches")
     _, k8, v8 = _expand_gpu_fp8(lkv, w, x, scale)
-    rope_codes = li.to_e4m3_bits(li.bf16_bits_to_f32(x["kv"][..., w.d_c:]).astype(np.float64) / scale)
+    P, bt, lens = w.page_size, x["block_table"], x["seqlens"]
+    S = int(lens.max())
+    rope = x["kv"][..., w.d_c:]
+    new = np.zeros((w.B, S, w.d_rope), np.uint16)
+    for b, L in enumerate(lens):
+        for t in range(S):
+            j = int(L) - S + t
+            if j >= 0:
+                new[b, t] = rope[bt[b, j // P], j % P]
+    rope8 = torch.full((x["num_pages"] * P * w.d_rope,), 0x7F, dtype=torch.uint8, device="cuda")
+    lkv.lkv_append_tokens(to_dev(new, torch), rope8, torch.from_numpy(bt).cuda(),
+                          torch.from_numpy(lens).cuda(), page_size=P, out_fp8=True, out_scale=scale)
+    rope_codes = rope8.cpu().numpy().reshape(x["num_pages"], P, w.d_rope)
+    valid = li.valid_slot_mask(bt, lens, P, x["num_pages"])
+    want = oracle.e4m3_from_f64(li.bf16_bits_to_f32(rope).astype(np.float64) / scale)
+    assert np.array_equal(rope_codes[valid], want[valid])
     out, lse = lkv.lkv_gqa_decode(to_dev(x["q_nope_h"], torch), to_dev(x["q_rope"], torch), k8, v8,
-                                  torch.from_numpy(np.ascontiguousarray(rope_codes)).cuda().reshape(-1),
-                                  torch.from_numpy(x["block_table"]).cuda(),
-                                  torch.from_numpy(x["seqlens"]).cuda(), n_kv=w.n_kv,
-                                  page_size=w.page_size, softmax_scale=w.scale,
+                                  rope8, torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda(),
+                                  n_kv=w.n_kv, page_size=P, softmax_scale=w.scale,
                                   rope_tok_stride=w.d_rope, kv_fp8=True, kv_scale=scale)
     rk, rv = oracle.expand_latent(x["kv"].reshape(-1), _w64(x, "w_uk"), _w64(x, "w_uv"),
                                   x["block_table"], x["seqlens"], page_size=w.page_size,
@@ -594,6 +608,37 @@ def test_append_tokens_bit_exact(lkv, oracle):
     ref = oracle.append_tokens(src, x["kv"], x["block_table"], x["seqlens"],
                                page_size=w.page_size, tok_stride=width)
     assert np.array_equal(got.view(np.uint16), ref.view(np.uint16).reshape(-1))
+
+
+@pytest.mark.parametrize("scale", [1.0 / 16, 0.37])
+def test_append_tokens_fp8_bit_exact(lkv, oracle, scale):
+    """8-bit cache write: each bf16 value x becomes the code of fl32(x *
+    fl32(1 / scale)).  Both sides round that float32 product (the oracle's
+    encoder takes it exactly), so the codes agree bit for bit -- special
+    values included (NaN, infinities, magnitudes past 448, subnormals); rows
+    of negative positions and untouched slots keep their bytes."""
+    rng = np.random.default_rng(912)
+    B, s_q, width, P = 3, 5, 64 + 32, 16
+    seqlens = np.array([40, 3, 17], np.int32)
+    npages = 12
+    bt = rng.permutation(npages)[: B * 4].reshape(B, 4).astype(np.int32)
+    x = (rng.standard_normal((B, s_q, width)) * 8).astype(np.float32)
+    x[0, 0, :6] = [np.nan, np.inf, -np.inf, 1000.0, -449.0, 2.0 ** -12]
+    x[1, 4, :4] = [-0.0, 2.0 ** -10, -(2.0 ** -9) * 1.5, 0.0]
+    src = li.to_bf16_bits(x)
+    cache0 = rng.integers(0, 256, (npages * P, width), dtype=np.uint8)
+    cache = torch.from_numpy(cache0.copy()).cuda()
+    note(f"case append fp8 scale={scale}")
+    lkv.lkv_append_tokens(to_dev(src, torch), cache, torch.from_numpy(bt).cuda(),
+                          torch.from_numpy(seqlens).cuda(), page_size=P, out_fp8=True,
+                          out_scale=scale)
+    torch.cuda.synchronize()
+    got = cache.cpu().numpy().reshape(-1)
+    inv = np.float32(1) / np.float32(scale)
+    prod = (li.bf16_bits_to_f32(src) * inv).astype(np.float32)
+    ref = oracle.append_tokens(oracle.e4m3_from_f64(prod.astype(np.float64)), cache0, bt,
+                               seqlens, page_size=P, tok_stride=width)
+    assert np.array_equal(got, ref.reshape(-1))
 
 
 def test_decode_layer_on_gpu(lkv, oracle):
