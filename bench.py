@@ -80,6 +80,20 @@ def measured_counters(workload: str):
     return c
 
 
+def counter_fields(workload: str):
+    """The attention kernel's matrix-unit busy fraction (SQ_VALU_MFMA_BUSY_CYCLES
+    over every SIMD's cycles at the published 2.4 GHz) and the fraction of
+    wave time spent waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES), from the committed
+    counter run of the same kernel source; None when there is none."""
+    c = measured_counters(workload)
+    if c is None or "busy" not in c:
+        return None
+    b = c["busy"]
+    return {"mfma_busy": b["mfma_busy_frac"], "wait_any": b["wait_any_frac"],
+            "duration_us": b["duration_ns"] / 1e3,
+            "source": f"profiles/{workload}_counters.json (rocprofv3 --pmc)"}
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch of the attention kernel (see measured_counters)."""
     c = measured_counters(workload)
@@ -574,11 +588,7 @@ def main():
                         "intensity": work.intensity},
         "parity_sample_rel_l2": rel,
     }
-    c = measured_counters(w.name)
-    if c is not None and "busy" in c:
-        # from the counter run of the same kernel source (rocprofv3 --pmc)
-        result["counters"] = {k: c["busy"][k] for k in
-                              ("mfma_busy_frac", "shader_clock_ghz", "wait_any_frac") if k in c["busy"]}
+    result["counters"] = counter_fields(w.name)
     result.update(s.get("extra", {}))
     if f32:
         result["note"] = ("a few kilobytes of cache per step: the kernel is bound by launch "

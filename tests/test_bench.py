@@ -63,3 +63,38 @@ def test_oracle_thread_count_can_be_set():
     assert oracle.num_threads() == 1
     oracle.set_num_threads(n)
     assert oracle.num_threads() == n
+
+
+def test_counter_fields_follow_the_kernel_source(tmp_path, monkeypatch):
+    """MFMA busy and traffic come from a committed counter summary only while
+    the kernel source it names is unchanged."""
+    import json
+    import bench
+    src = tmp_path / "k.hip"
+    src.write_text("kernel v1")
+    c = {"kernel_source": str(src), "kernel_source_sha": bench.source_sha(str(src)),
+         "hbm_bytes_per_launch": 123.0,
+         "busy": {"mfma_busy_frac": 0.25, "wait_any_frac": 0.5, "duration_ns": 9000.0}}
+    (tmp_path / "w_counters.json").write_text(json.dumps(c))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    monkeypatch.setattr(bench, "ROOT", "/")
+    f = bench.counter_fields("w")
+    assert f["mfma_busy"] == 0.25 and f["wait_any"] == 0.5 and f["duration_us"] == 9.0
+    assert bench.measured_traffic("w") == 123.0
+    src.write_text("kernel v2")
+    assert bench.counter_fields("w") is None and bench.measured_traffic("w") is None
+    assert bench.counter_fields("absent") is None
+
+
+def test_committed_counter_summaries_name_a_source():
+    """Every committed counter summary names an existing kernel source and
+    carries the busy figures."""
+    import glob
+    import json
+    import bench
+    files = glob.glob(os.path.join(ROOT, "profiles", "*_counters.json"))
+    assert files
+    for f in files:
+        c = json.load(open(f))
+        assert os.path.isfile(os.path.join(ROOT, c["kernel_source"])), f
+        assert {"mfma_busy_frac", "wait_any_frac"} <= set(c["busy"]), f
