@@ -125,6 +125,56 @@ class HipEvents:
         self.hip.hipEventDestroy(self.ct.c_void_p(e))
 
 
+def ramp(workload: str, n: int):
+    """Per-step times from a cold start, an event pair around every step: first
+    a plain device copy as large as the workload's cache (four rotating
+    buffers), then the decode step itself.  Prints one JSON line with the
+    medians of each block of 25 steps, which shows whether a slow start
+    belongs to the chip (the copy slows too) or to the decode kernel."""
+    import torch
+    import latent_kv_decode_amd as lkv
+    import lkv_inputs as li
+    from latent_kv_decode_amd import roofline as rf
+    lkv.load_library()
+    stream = torch.cuda.current_stream()
+
+    def series(fn):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            ev[i][0].record(stream)
+            fn(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        return [round(float(np.median(us[i:i + 25])), 1) for i in range(0, n, 25)]
+
+    w = li.workload(workload)
+    x = li.generate(w)
+    nbytes = sum(int(v.nbytes) for k, v in x.items() if k in ("kv", "k_cache", "v_cache"))
+    src = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    dst = [torch.empty_like(t) for t in src]
+    for t in src:
+        t.fill_(1)
+    torch.cuda.synchronize()
+    time.sleep(2.0)
+    log(f"[bench] ramp: copy of {nbytes} bytes, {n} steps")
+    cp = series(lambda i: dst[i % 4].copy_(src[i % 4]))
+    del src, dst
+
+    class Opt:
+        num_splits = 0
+
+    s = SETUPS[w.kind](w, x, Opt, torch, lkv, rf)
+    torch.cuda.synchronize()
+    time.sleep(2.0)
+    log(f"[bench] ramp: {w.name} step, {n} steps")
+    st = series(lambda i: s["step"](i))
+    print(json.dumps({"ramp": w.name, "steps": n, "block": 25, "copy_bytes": nbytes,
+                      "copy_us_median_per_block": cp, "step_us_median_per_block": st}), flush=True)
+
+
 def calibrate_copy(steps):
     """A plain 1 GiB device copy, `steps` times: FETCH_SIZE and WRITE_SIZE of
     this kernel in a rocprofv3 run give the counters' bytes-per-unit scale."""
@@ -483,6 +533,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--ramp", type=int, default=0,
+                    help="per-step times of a copy and of the step from a cold start, N steps each")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -491,6 +543,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.steps if args.steps != 200 else 5)
+        return
+    if args.ramp:
+        ramp(args.workload, args.ramp)
         return
 
     import torch

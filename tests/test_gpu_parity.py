@@ -275,6 +275,26 @@ def _gqa_small(seed, *, B=3, h_q=32, n_kv=8, d_h=128, d_rope=0, s_q=1, seqlens=(
     return w, li.generate(w)
 
 
+@pytest.mark.parametrize("h_q,n_kv,d_h,d_rope,s_q,causal,seqlens", [
+    (8, 2, 64, 0, 1, True, (100, 700, 65)),
+    (16, 4, 32, 8, 2, True, (0, 1, 130, 64)),       # empty and one-token rows
+    (8, 1, 128, 16, 3, False, (300, 5, 1000)),      # many tiles per wave
+    (32, 8, 16, 0, 1, True, (17, 250))])
+def test_fp32_gqa(lkv, oracle, h_q, n_kv, d_h, d_rope, s_q, causal, seqlens):
+    """The float32 kernel over separate K and V caches (the value rows are
+    staged beside the keys), with and without a shared RoPE key."""
+    w = li.Workload(name="g", kind="gqa", dtype="f32", B=len(seqlens), h_q=h_q, s_q=s_q,
+                    page_size=16, n_kv=n_kv, d_h=d_h, d_rope=d_rope, seqlens=tuple(seqlens),
+                    table="shuffled", causal=causal, scale=1 / math.sqrt(d_h + d_rope),
+                    seed=1700 + h_q + d_h)
+    x = li.generate(w)
+    assert x["q"].dtype == np.float32
+    note(f"case fp32 gqa h_q={h_q} n_kv={n_kv} d_h={d_h} d_rope={d_rope} s_q={s_q} causal={causal}")
+    out, lse = _run_gqa(lkv, w, x)
+    ro, rl = _oracle_gqa(oracle, w, x)
+    assert_close(from_dev(out), ro, from_dev(lse), rl, f32=True, what="fp32 gqa")
+
+
 def _run_gqa(lkv, w, x, **kw):
     dev = {k: to_dev(x[k], torch) for k in ("q", "k_cache", "v_cache")}
     qr = to_dev(x["q_rope"], torch) if w.d_rope else None
