@@ -22,10 +22,9 @@
 // the value waves issue their share of a tile before their products, the
 // score waves after theirs.
 //
-// 8-bit (E4M3) cache: the score waves load a tile's codes into registers one
-// iteration before it is needed (two register sets), convert them to bf16 and
-// write them in the same ring slot layout, so the products read bf16 as
-// above.  Each code is converted once per work-group; the cache bytes read
+// 8-bit (E4M3) cache: the score waves load the next tile's codes into
+// registers before their products, then convert them to bf16 and write them
+// in the same ring slot layout, so the products read bf16 as above.  Each code is converted once per work-group; the cache bytes read
 // are halved.  The value waves, whose accumulators fill their registers, do
 // no staging.
 #include <type_traits>
@@ -438,7 +437,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
       constexpr int NPL = F8 && kScore ? 8 * PPR / 64 : 0;
       constexpr bool kRopeStage = F8 && kScore && DR > 0;
       static_assert(!F8 || 8 * PPR % 64 == 0, "8-bit staging");
-      u32x4 stg[2][NPL + 1];
+      u32x4 stg[1][NPL + 1];  // one register set
       auto row_of = [&](int t) -> long long {
         return dma_al ? (long long)__builtin_amdgcn_readlane(dma_rows, 0) + t : (long long)__shfl(dma_rows, t);
       };
@@ -605,21 +604,17 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
         return I == 0 ? s_b0 : I == 1 ? s_b1 : I == 2 ? s_b2 : s_b3;
       };
       // prologue: tiles k0 and k0 + 1 (a sequence with no token zero-fills).
-      // 8-bit cache: tile k0 goes to slot 0 now, tile k0 + 1 waits in
-      // register set 1 (stored at the end of the first iteration).
+      // 8-bit cache: tile k0 goes to slot 0 now; tile k0 + 1 is loaded and
+      // stored by the first iteration.
       if constexpr (F8) {
         if (L > 0) {
           if constexpr (kScore) {
             dma_prepare(k0, true);
             stage_load(std::integral_constant<int, 0>{});
-            dma_prepare(k0 + 1, true);
-            stage_load(std::integral_constant<int, 1>{});
             stage_store(std::integral_constant<int, 0>{}, s_b0);
           }
         } else {
           zero_tile(s_b0);
-#pragma unroll
-          for (int i = 0; i <= NPL; ++i) stg[1][i] = u32x4{0u, 0u, 0u, 0u};
         }
       } else {
         if (L > 0) {
@@ -643,16 +638,16 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
         constexpr int R = decltype(r_tag)::value;  // (k - k0) mod 4
         constexpr bool kFirst = decltype(first_tag)::value;
         if constexpr (F8) {
-          // score waves: tile k + 2 into register set R mod 2 (issued before
-          // the products, so a load has about two iterations to land), tile
-          // k + 1 (set R + 1 mod 2) into ring slot R + 1, whose last tile
-          // (k - 3) was read two iterations ago
-          constexpr int SN = R & 1, SP = SN ^ 1;
+          // score waves: tile k + 1 into registers (issued before the
+          // products, which give the loads their time to land), then into
+          // ring slot R + 1, whose last tile (k - 3) was read two iterations
+          // ago.  One register set: a second set (loads two tiles ahead)
+          // measured the same and spilled in the ring loop.
           if constexpr (kScore) {
-            dma_prepare(k + 2, k + 2 < k1 && L > 0);
-            stage_load(std::integral_constant<int, SN>{});
+            dma_prepare(k + 1, k + 1 < k1 && L > 0);
+            stage_load(std::integral_constant<int, 0>{});
             if (k < k1) score_tile(buf_of(std::integral_constant<int, R>{}), k);
-            stage_store(std::integral_constant<int, SP>{}, buf_of(std::integral_constant<int, (R + 1) % kRing>{}));
+            stage_store(std::integral_constant<int, 0>{}, buf_of(std::integral_constant<int, (R + 1) % kRing>{}));
           } else {
             if constexpr (!kFirst) value_tile(buf_of(std::integral_constant<int, (R + kRing - 1) % kRing>{}), k - 1);
           }
