@@ -12,17 +12,20 @@
 // outputs scattered to) cache rows through the block table.
 //
 // A work-group computes a 256-token x 256-column tile of D over K-chunks of
-// 64 (double-buffered in LDS, the next chunk prefetched into registers while
-// the current one is multiplied).  Eight waves: wave w takes tokens
-// 128 (w mod 2) .. and columns 64 (w / 2) .. of the tile and computes
-// D^T = W^T C^T with v_mfma_f32_16x16x32_bf16 (A = W^T from the row-major
-// weight chunk through ds_read_b64_tr_b16, B = C^T read row-wise from the
-// token chunk): 32 products per 32-deep k-step for 12 fragment reads.  The
-// column tiles of one token tile run on one XCD, so that its latent rows are
-// read from HBM once.  float32 accumulation, bf16 output (round to nearest
-// even).  The finished tile goes through the (then free) staging LDS in
-// row-major order, so that each token's columns leave as whole 16-byte
-// pieces of contiguous runs rather than as scattered 8-byte stores.
+// 32, brought into LDS by direct-to-LDS loads through a ring of four stages,
+// three chunks ahead of the products (every wave issues four 1-KiB loads per
+// chunk and waits only for the chunk it is about to read, then one barrier).
+// Eight waves: wave w takes tokens 128 (w mod 2) .. and columns 64 (w / 2) ..
+// of the tile and computes D^T = W^T C^T with v_mfma_f32_16x16x32_bf16 (A =
+// W^T from the row-major weight chunk through ds_read_b64_tr_b16, B = C^T
+// read row-wise from the token chunk): 32 products per chunk for 12 fragment
+// reads.  The column tiles of one token tile run on one XCD, so that its
+// latent rows are read from HBM once.  float32 accumulation, bf16 output
+// (round to nearest even).  The finished tile goes through the (then free)
+// stages in row-major order, so that each token's columns leave as whole
+// 16-byte pieces of contiguous runs, with streaming stores (the output is
+// not read again here, and in the cache it would push out the latent rows
+// the other column tiles still read).
 #include "e4m3.h"
 #include "lkv_internal.h"
 
@@ -39,17 +42,20 @@ typedef __bf16 bf16;
 constexpr int kMaxDc = 512;
 constexpr int kTM = 256;        // tokens per work-group
 constexpr int kTN = 256;        // output columns per work-group
-constexpr int kKC = 64;         // K-chunk
 constexpr int kThreadsX = 512;  // 8 waves
+constexpr int kKC = 32;         // K-chunk
+constexpr int kStage = kTM * kKC + kKC * kTN;  // bf16 elements per stage (32 KiB)
 
-// Token chunk [256][64]: rows of 8 sixteen-byte chunks; chunk c of row r at
-// c ^ ((r / 2) mod 8), so that sixteen rows read at one chunk column hit
-// distinct banks.
-__device__ __forceinline__ int swz_c(int c, int r) { return c ^ ((r >> 1) & 7); }
-// Weight chunk [64][256]: rows of 32 chunks (512 bytes, one full pass over
+// Token chunk [256][32]: rows of 4 sixteen-byte pieces; piece c of row r at
+// slot c ^ ((r / 2) mod 4).  Chosen by measurement (SQ_LDS_BANK_CONFLICT):
+// with this pattern the B-operand reads (16 rows, pieces g = 0..3) add no
+// bank conflicts, where no swizzle, r mod 4 or (r / 4) mod 4 add 33 M
+// conflict cycles per launch at the GQLA g = 8 shape.
+__device__ __forceinline__ int swz_t(int c, int r) { return c ^ ((r >> 1) & 3); }
+// Weight chunk [32][256]: rows of 32 pieces (512 bytes, one full pass over
 // the banks, so every row starts on bank 0).  A transpose read covers rows
-// 8g + (0..3) and + 4 for g = 0..3 at one chunk pair: the low three chunk
-// bits take a bijection of r mod 8 and chunk bits 3..4 take (r / 8) mod 4,
+// 8g + (0..3) and + 4 for g = 0..3 at one piece pair: the low three piece
+// bits take a bijection of r mod 8 and piece bits 3..4 take (r / 8) mod 4,
 // which puts the rows of one read on distinct banks.
 __device__ __forceinline__ int swz_w(int c, int r) {
   const int t = r & 7;
@@ -62,22 +68,23 @@ __device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Stage layout: token chunk, then weight chunk.  One wave instruction fills
+// 1 KiB of a stage in lane order; lane i fetches the piece whose swizzled
+// slot is i, so the swizzle costs nothing at store time.
 template <int DH>
 __global__ void __launch_bounds__(kThreadsX) expand_kernel(const ExpandParams p) {
   static_assert(kTN % DH == 0 || DH % kTN == 0, "column tile and group width");
-  // staging buffers (token and weight chunks, double-buffered), reused at
-  // the end for the bf16 output tile [kTM][kTN]
-  static_assert(2 * kTM * kKC + 2 * kKC * kTN == kTM * kTN, "output tile fits the staging LDS");
-  __shared__ __attribute__((aligned(16))) bf16 s_mem[2 * kTM * kKC + 2 * kKC * kTN];
-  bf16(*s_c)[kTM * kKC] = reinterpret_cast<bf16(*)[kTM * kKC]>(s_mem);
-  bf16(*s_w)[kKC * kTN] = reinterpret_cast<bf16(*)[kKC * kTN]>(s_mem + 2 * kTM * kKC);
+  static_assert(4 * kStage == kTM * kTN, "output tile fits the four stages");
+  __shared__ __attribute__((aligned(16))) bf16 s_st0[kStage];
+  __shared__ __attribute__((aligned(16))) bf16 s_st1[kStage];
+  __shared__ __attribute__((aligned(16))) bf16 s_st2[kStage];
+  __shared__ __attribute__((aligned(16))) bf16 s_st3[kStage];
   __shared__ int s_row[kTM];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, n = lane & 15;
-  // block -> (token tile, column tile); the column tiles of one token tile
-  // share an XCD (block index mod 8)
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int ncols = 2 * p.g * DH;
-  const int n_ct = (ncols + kTN - 1) / kTN;  // the last tile may be partial
+  const int n_ct = (ncols + kTN - 1) / kTN;
   const int tiles_per_seq = (p.max_pages * p.page_size + kTM - 1) / kTM;
   const int bx = blockIdx.x;
   const int rest = bx >> 3;
@@ -95,50 +102,42 @@ __global__ void __launch_bounds__(kThreadsX) expand_kernel(const ExpandParams p)
   }
   __syncthreads();
 
-  // ---- staging: thread tid moves sixteen-byte pieces tid + 512 u (u < 4)
-  // of the token chunk (piece i: token i / 8, chunk i mod 8) and of the
-  // weight chunk (row i / 32, column chunk i mod 32), K-chunk kc: eight
-  // consecutive lanes read one token's 128 bytes, thirty-two one weight
-  // row's 512.
-  const bf16 *cbase = static_cast<const bf16 *>(p.c);
+  // ---- this wave's loads: token rows 32 wu + 16 u + lane / 4 (piece slot
+  // lane mod 4) and weight rows 4 wu + 2 u + lane / 32 (slot lane mod 32),
+  // u = 0, 1.  Invalid tokens read row 0 (their outputs are not written);
+  // columns past the last group read the first weight row.
   const int col0 = ct * kTN;
-  const int a_ch = tid & 7, w_ch = tid & 31;
-  int a_row[4];
+  const char *tsrc[2];
+  const char *wsrc[2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) a_row[u] = s_row[(tid + 512 * u) >> 3];
-  // weight column chunk -> (block, offset): column 8 w_ch of the tile
-  const int w_col = col0 + 8 * w_ch;
-  const int w_blk = w_col / DH, w_d = w_col % DH;
-  const bf16 *w_mat = static_cast<const bf16 *>(w_blk < p.g ? p.w_uk : p.w_uv) +
-                      (long long)(w_blk % p.g) * p.d_c * DH + w_d;
-  u32x4 pa[4], pw[4];
-  auto load_chunk = [&](int kc) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (a_row[u] >= 0)
-        v = *reinterpret_cast<const u32x4 *>(cbase + (long long)a_row[u] * p.c_stride + kc * kKC + 8 * a_ch);
-      pa[u] = v;
+  for (int u = 0; u < 2; ++u) {
+    const int r = 32 * wu + 16 * u + (lane >> 2);
+    const int row = max(s_row[r], 0);
+    const int c = swz_t(lane & 3, r);
+    tsrc[u] = reinterpret_cast<const char *>(static_cast<const bf16 *>(p.c) + (long long)row * p.c_stride + 8 * c);
+    const int kr = 4 * wu + 2 * u + (lane >> 5);
+    const int cw = swz_w(lane & 31, kr);
+    const int col = col0 + 8 * cw;
+    const bf16 *wm = static_cast<const bf16 *>(p.w_uk);
+    long long off = 0;
+    if (col < ncols) {
+      const int blk = col / DH, d = col % DH;
+      wm = static_cast<const bf16 *>(blk < p.g ? p.w_uk : p.w_uv);
+      off = (long long)(blk % p.g) * p.d_c * DH + d;
     }
+    wsrc[u] = reinterpret_cast<const char *>(wm + off + (long long)kr * DH);
+  }
+  auto issue = [&](int kc, bf16 *st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = kc * kKC + ((tid + 512 * u) >> 5);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (w_col < ncols) v = *reinterpret_cast<const u32x4 *>(w_mat + (long long)k * DH);
-      pw[u] = v;
-    }
-  };
-  auto store_chunk = [&](int buf) {
+    for (int u = 0; u < 2; ++u)
+      __builtin_amdgcn_global_load_lds(tsrc[u] + kc * (kKC * 2),
+                                       (__attribute__((address_space(3))) void *)(st + (32 * wu + 16 * u) * kKC),
+                                       16, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int tok = (tid + 512 * u) >> 3;
-      *reinterpret_cast<u32x4 *>(&s_c[buf][tok * kKC + swz_c(a_ch, tok) * 8]) = pa[u];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = (tid + 512 * u) >> 5;
-      *reinterpret_cast<u32x4 *>(&s_w[buf][r * kTN + swz_w(w_ch, r) * 8]) = pw[u];
-    }
+    for (int u = 0; u < 2; ++u)
+      __builtin_amdgcn_global_load_lds(wsrc[u] + (long long)kc * (kKC * DH * 2),
+                                       (__attribute__((address_space(3))) void *)(st + kTM * kKC + (4 * wu + 2 * u) * kTN),
+                                       16, 0, 0);
   };
 
   // ---- this wave's share: tokens 128 wt + 16 nt + n, columns 64 wc + 16 mt
@@ -148,63 +147,92 @@ __global__ void __launch_bounds__(kThreadsX) expand_kernel(const ExpandParams p)
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nkc = p.d_c / kKC;
-  load_chunk(0);
-  store_chunk(0);
-  __syncthreads();
-  for (int kc = 0; kc < nkc; ++kc) {
-    const int buf = kc & 1;
-    if (kc + 1 < nkc) load_chunk(kc + 1);
-    const bf16 *ct_ = s_c[buf];
-    const bf16 *wt_ = s_w[buf];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      // B = C^T: token 128 wt + 16 nt + n, K 32 ks + 8 g .. + 7
-      bf16x8 bc[8];
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int tok = 128 * wt + 16 * nt + n;
-        bc[nt] = *reinterpret_cast<const bf16x8 *>(ct_ + tok * kKC + swz_c(4 * ks + g, tok) * 8);
-      }
-      // A = W^T: column 64 wc + 16 mt + 4 (n mod 4) .. + 3 of weight rows
-      // rk and rk + 4
-      const int rk = 32 * ks + 8 * g + (n >> 2);
-      bf16x8 aw[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int col = 64 * wc + 16 * mt + 4 * (n & 3);
-        const int ch = col >> 3, off = col & 7;
-        aw[mt] = join(lds_read_tr(wt_ + rk * kTN + swz_w(ch, rk) * 8 + off),
-                      lds_read_tr(wt_ + (rk + 4) * kTN + swz_w(ch, rk + 4) * 8 + off));
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[mt], bc[nt], acc[mt][nt], 0, 0, 0);
-    }
-    // the other buffer was last read in the previous chunk, before the
-    // barrier that ended it
-    if (kc + 1 < nkc) store_chunk(buf ^ 1);
-    __syncthreads();
-  }
-
-  if (p.out_fp8) {
-    // ---- 8-bit caches: codes of value * (1 / out_scale), rounded once from
-    // the float32 results, into LDS as a [token][column] byte tile (16-byte chunk
-    // c of token row t at c ^ (t mod 16)), then out in 16-byte pieces
-    unsigned char *s8 = reinterpret_cast<unsigned char *>(s_mem);
+  auto compute = [&](const bf16 *st) __attribute__((always_inline)) {
+    const bf16 *ct_ = st;
+    const bf16 *wt_ = st + kTM * kKC;
+    bf16x8 bc[8];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
       const int tok = 128 * wt + 16 * nt + n;
+      bc[nt] = *reinterpret_cast<const bf16x8 *>(ct_ + tok * kKC + swz_t(g, tok) * 8);
+    }
+    const int rk = 8 * g + (n >> 2);
+    bf16x8 aw[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int col = 64 * wc + 16 * mt + 4 * (n & 3);
+      const int ch = col >> 3, off = col & 7;
+      aw[mt] = join(lds_read_tr(wt_ + rk * kTN + swz_w(ch, rk) * 8 + off),
+                    lds_read_tr(wt_ + (rk + 4) * kTN + swz_w(ch, rk + 4) * 8 + off));
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[mt], bc[nt], acc[mt][nt], 0, 0, 0);
+  };
+  // barrier without the global-memory fence of __syncthreads() (which would
+  // wait for every load in flight): each wave has waited for its own loads
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // Every step issues one chunk (past the last chunk, a copy of the last
+  // one into a stage that is not read again), so this wave always has the
+  // same count of loads in flight: chunk kc has landed once at most 8 (the
+  // next two chunks) remain.
+  const int nkc = p.d_c / kKC;
+  issue(0, s_st0);
+  issue(min(1, nkc - 1), s_st1);
+  issue(min(2, nkc - 1), s_st2);
+  auto step = [&](auto r_tag, int kc) __attribute__((always_inline)) {
+    constexpr int R = decltype(r_tag)::value;
+    bf16 *cur = R == 0 ? s_st0 : R == 1 ? s_st1 : R == 2 ? s_st2 : s_st3;
+    bf16 *nxt = R == 0 ? s_st3 : R == 1 ? s_st0 : R == 2 ? s_st1 : s_st2;  // stage of chunk kc + 3
+    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    barrier();
+    issue(min(kc + 3, nkc - 1), nxt);
+    compute(cur);
+  };
+  int kc = 0;
+  for (; kc + 4 <= nkc; kc += 4) {
+    step(std::integral_constant<int, 0>{}, kc);
+    step(std::integral_constant<int, 1>{}, kc + 1);
+    step(std::integral_constant<int, 2>{}, kc + 2);
+    step(std::integral_constant<int, 3>{}, kc + 3);
+  }
+  if (kc < nkc) {
+    step(std::integral_constant<int, 0>{}, kc);
+    if (kc + 1 < nkc) {
+      step(std::integral_constant<int, 1>{}, kc + 1);
+      if (kc + 2 < nkc) step(std::integral_constant<int, 2>{}, kc + 2);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();  // every stage read; the stages take the output tile
+
+  // output tile row-major over the four stages: token t at stage t / 64
+  auto orow = [&](int tok) -> bf16 * {
+    const int q = tok >> 6;
+    bf16 *st = q == 0 ? s_st0 : q == 1 ? s_st1 : q == 2 ? s_st2 : s_st3;
+    return st + (tok & 63) * kTN;
+  };
+  if (p.out_fp8) {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const int tok = 128 * wt + 16 * nt + n;
+      const int q = tok >> 7;  // 8-bit tile: token t at stage t / 128, 256 bytes per row
+      unsigned char *base8 = reinterpret_cast<unsigned char *>(q == 0 ? s_st0 : s_st1) + (tok & 127) * kTN;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int col = 64 * wc + 16 * mt + 4 * g;
         unsigned word = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) word |= e4m3_encode(acc[mt][nt][i] * p.out_inv_scale) << (8 * i);
-        *reinterpret_cast<unsigned *>(s8 + tok * kTN + (((col >> 4) ^ (tok & 15)) << 4) + (col & 15)) = word;
+        *reinterpret_cast<unsigned *>(base8 + (((col >> 4) ^ (tok & 15)) << 4) + (col & 15)) = word;
       }
     }
     __syncthreads();
@@ -214,23 +242,19 @@ __global__ void __launch_bounds__(kThreadsX) expand_kernel(const ExpandParams p)
       const int row = s_row[tok];
       const int col = col0 + 16 * c;
       if (row < 0 || col >= ncols) continue;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(s8 + tok * kTN + ((c ^ (tok & 15)) << 4));
+      const unsigned char *base8 = reinterpret_cast<const unsigned char *>((tok >> 7) == 0 ? s_st0 : s_st1) + (tok & 127) * kTN;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(base8 + ((c ^ (tok & 15)) << 4));
       const int blk = col / DH, d = col % DH;
       unsigned char *dst = static_cast<unsigned char *>(blk < p.g ? p.k_out : p.v_out);
       const long long ostride = blk < p.g ? p.k_stride : p.v_stride;
-      *reinterpret_cast<u32x4 *>(dst + (long long)row * ostride + (long long)(blk % p.g) * DH + d) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst + (long long)row * ostride + (long long)(blk % p.g) * DH + d));
     }
     return;
   }
-
-  // ---- D^T tile (columns 4 g .. + 3 of token n per lane) into LDS as a
-  // row-major [token][column] bf16 tile; 16-byte chunk c of token row t at
-  // c ^ 2 (t mod 16), so that the 16 tokens x 4 column groups of one write
-  // hit distinct banks.  (The loop's last barrier ended every read of the
-  // staging buffers.)
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
     const int tok = 128 * wt + 16 * nt + n;
+    bf16 *r = orow(tok);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int col = 64 * wc + 16 * mt + 4 * g;
@@ -238,23 +262,21 @@ __global__ void __launch_bounds__(kThreadsX) expand_kernel(const ExpandParams p)
       bf16x4 o;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = static_cast<bf16>(acc[mt][nt][i]);
-      *reinterpret_cast<bf16x4 *>(s_mem + tok * kTN + ch * 8 + (col & 7)) = o;
+      *reinterpret_cast<bf16x4 *>(r + ch * 8 + (col & 7)) = o;
     }
   }
   __syncthreads();
-  // ---- out: piece q = tid + 512 u is chunk q mod 32 (8 columns) of token
-  // row q / 32; half a wave covers one token's 512 bytes
 #pragma unroll 4
   for (int u = 0; u < kTM * kTN / 8 / kThreadsX; ++u) {
     const int q = tid + kThreadsX * u, tok = q >> 5, c = q & 31;
     const int row = s_row[tok];
     const int col = col0 + 8 * c;
     if (row < 0 || col >= ncols) continue;
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(s_mem + tok * kTN + ((c ^ ((tok & 15) << 1)) * 8));
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(orow(tok) + ((c ^ ((tok & 15) << 1)) * 8));
     const int blk = col / DH, d = col % DH;
     bf16 *dst = static_cast<bf16 *>(blk < p.g ? p.k_out : p.v_out);
     const long long ostride = blk < p.g ? p.k_stride : p.v_stride;
-    *reinterpret_cast<u32x4 *>(dst + (long long)row * ostride + (long long)(blk % p.g) * DH + d) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst + (long long)row * ostride + (long long)(blk % p.g) * DH + d));
   }
 }
 
