@@ -360,18 +360,22 @@ def _w64(x, k):
     return li.bf16_bits_to_f32(x[k]).astype(np.float64)
 
 
-@pytest.mark.parametrize("g,d_c,d_h,seqlens", [
-    (8, 512, 128, (130, 64)),
+@pytest.mark.parametrize("g,d_c,d_h,seqlens,page", [
+    (8, 512, 128, (130, 64), 64),
     # three groups of 64 (a partial 256-column tile), one group of 256,
     # sequences spanning several 256-token tiles with ragged ends
-    (3, 256, 64, (600, 257, 1)), (1, 128, 256, (300, 513))])
-def test_expand_matches_oracle(lkv, oracle, g, d_c, d_h, seqlens):
+    (3, 256, 64, (600, 257, 1), 64), (1, 128, 256, (300, 513), 64),
+    # latent widths whose count of 32-wide K-chunks is not a multiple of the
+    # four-stage ring (2, 6, 14 chunks), pages of 16, 48 and 1000 tokens
+    (2, 64, 128, (300, 17), 16), (4, 192, 64, (500, 96, 257), 48),
+    (1, 448, 256, (1001, 3), 1000)])
+def test_expand_matches_oracle(lkv, oracle, g, d_c, d_h, seqlens, page):
     w = li.Workload(name="gqla", kind="gqla", dtype="bf16", B=len(seqlens), h_q=16 * g, s_q=1,
-                    page_size=64, n_lat=1, d_c=d_c, n_kv=g, d_h=d_h, d_rope=64,
+                    page_size=page, n_lat=1, d_c=d_c, n_kv=g, d_h=d_h, d_rope=64,
                     seqlens=tuple(seqlens), table="shuffled", scale=1 / math.sqrt(d_h + 64),
-                    seed=700 + g)
+                    seed=700 + g + d_c)
     x = li.generate(w)
-    note(f"case expand g={g} d_c={d_c} d_h={d_h} seqlens={seqlens}")
+    note(f"case expand g={g} d_c={d_c} d_h={d_h} seqlens={seqlens} page={page}")
     _, k_out, v_out = _expand_gpu(lkv, w, x)
     rk, rv = oracle.expand_latent(x["kv"].reshape(-1), _w64(x, "w_uk"), _w64(x, "w_uv"),
                                   x["block_table"], x["seqlens"], page_size=w.page_size,
@@ -403,7 +407,8 @@ def _expand_gpu_fp8(lkv, w, x, scale):
     (1, 128, 256, (300, 513), 1.0 / 16),
     # a scale that is not a power of two: the float32 product with the
     # float32 reciprocal rounds once more (2^-24 relative) before the encoding
-    (8, 512, 128, (130, 64), 0.37), (3, 256, 64, (600, 257, 1), 0.37)])
+    (8, 512, 128, (130, 64), 0.37), (3, 256, 64, (600, 257, 1), 0.37),
+    (4, 192, 64, (500, 96, 257), 1.0 / 16)])
 def test_expand_fp8_codes(lkv, oracle, g, d_c, d_h, seqlens, scale):
     """8-bit expanded caches: the kernel rounds its float32 result, the
     oracle its fp64 one, so the codes agree except where a value lies within
