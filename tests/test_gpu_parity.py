@@ -931,6 +931,45 @@ def test_decode_calls_replay_under_a_hip_graph(lkv):
         assert torch.equal(gout.view(torch.int16), ref_g.view(torch.int16)), r
 
 
+def test_default_workspace_per_stream(lkv):
+    """Calls that pass no workspace use a cached buffer per (device, stream):
+    decodes on two streams at once, with plans that need more workspace
+    call after call, give the same bits as the same calls one at a time
+    with their own workspaces."""
+    cases = []
+    for i, (B, splits) in enumerate([(2, 3), (4, 7), (8, 16), (16, 40)]):
+        w, x = small_mla(2000 + i, B=B, seqlens=[300 + 97 * j for j in range(B)], table="shuffled")
+        cases.append((w, x, mla_device_inputs(x, w, torch), splits))
+    refs = []
+    for w, x, d, splits in cases:
+        need = lkv.lkv_mla_decode_workspace_size(d["q_nope"], d["q_rope"], d["c_kv"], d["k_rope"],
+                                                 d["block_table"], d["seqlens"], n_latent=w.n_lat,
+                                                 page_size=w.page_size, softmax_scale=w.scale,
+                                                 causal=w.causal, kv_tok_stride=d["kv_tok_stride"],
+                                                 rope_tok_stride=d["rope_tok_stride"],
+                                                 num_splits=splits)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        o, l = run_mla(lkv, w, d, num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        refs.append((o.clone(), l.clone()))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    got = []
+    note("case default workspace on two streams")
+    for r in range(2):
+        for i in range(len(cases)):
+            for s, j in ((s1, i), (s2, len(cases) - 1 - i)):
+                w, x, d, splits = cases[j]
+                with torch.cuda.stream(s):
+                    got.append((j, *run_mla(lkv, w, d, num_splits=splits)))
+    torch.cuda.synchronize()
+    for j, o, l in got:
+        assert torch.equal(o.view(torch.int16), refs[j][0].view(torch.int16)), j
+        assert torch.equal(l, refs[j][1]), j
+    keys = {k for k in lkv._workspaces if k[1] in (s1.cuda_stream, s2.cuda_stream)}
+    assert len(keys) == 2
+
+
 # ----------------------------------------------------- softmax normalisation
 def _pages_of(x, b, page):
     L = int(x["seqlens"][b])
