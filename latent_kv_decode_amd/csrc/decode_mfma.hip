@@ -86,7 +86,7 @@ __device__ __forceinline__ int swz(int chunk, int row) {
 // lane order) with 64 / CPT whole token rows; lane i fetches the chunk whose
 // swizzled slot is i, so the XOR layout costs nothing at store time.
 // row_reg: lane t holds the cache row of token t of the tile.
-template <int CPT>
+template <int CPT, int AUX = 0>
 __device__ __forceinline__ void dma_region(const bf16 *gbase, long long stride, bf16 *region,
                                            int row_reg, int w, int lane) {
   static_assert(CPT >= 8 && CPT <= 64 && CPT % 8 == 0, "chunks per token");
@@ -105,7 +105,7 @@ __device__ __forceinline__ void dma_region(const bf16 *gbase, long long stride, 
     const int ch = swz<CPT>(lane % CPT, tok);
     const bf16 *src = gbase + (long long)row * stride + ch * 8;
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(region + t0 * CPT * 8),
-                                     16, 0, 0);
+                                     16, 0, AUX);
   }
 }
 
@@ -127,6 +127,7 @@ struct ContigDma {
       loff[v] = tin * (int)stride * 2 + swz<CPT>(lane % CPT, tok) * 16;
     }
   }
+  template <int AUX = 0>
   __device__ __forceinline__ void issue(const bf16 *base, long long stride, bf16 *region, int wu) const {
     const char *bw = reinterpret_cast<const char *>(base) + (long long)(wu * TPI) * stride * 2;
     bf16 *rw = region + wu * TPI * CPT * 8;
@@ -134,7 +135,7 @@ struct ContigDma {
     for (int u = 0; u < CPT / 4; ++u) {
       const char *src = bw + (long long)(4 * u * TPI) * stride * 2 + loff[u & 3];
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(rw + 4 * u * TPI * CPT * 8),
-                                       16, 0, 0);
+                                       16, 0, AUX);
     }
   }
 };
@@ -308,6 +309,10 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
   const char *__restrict__ vc8 = static_cast<const char *>(p.v) + (long long)kvh * DV;
   // a 64-token tile never straddles a page when pages are a power of two >= 64
   const bool aligned_pages = p.page_shift >= 6;
+  // a row group with one row tile reads each key/value tile once: those
+  // loads stream (non-temporal), leaving the cache to what several
+  // work-groups read (the shared RoPE key)
+  const bool stream_kv = p.row_tiles == 1;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   ContigDma<DK / 8> dk_;
   ContigDma<DV / 8> dv_;
@@ -495,6 +500,9 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
         const long long row0 = (long long)pg * p.page_size + (jb & (p.page_size - 1));
         if constexpr (F8) {
           load_tile8(row0, 0);
+        } else if (stream_kv) {
+          dk_.template issue<2>(kc + row0 * p.k_stride, p.k_stride, buf, wu);
+          if constexpr (!VA) dv_.template issue<2>(vc + row0 * p.v_stride, p.v_stride, buf + C::VOFF, wu);
         } else {
           dk_.issue(kc + row0 * p.k_stride, p.k_stride, buf, wu);
           if constexpr (!VA) dv_.issue(vc + row0 * p.v_stride, p.v_stride, buf + C::VOFF, wu);
@@ -509,6 +517,9 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_decode_kernel(const DecodePa
         const int rr = j < L ? pg * p.page_size + slot_of(j) : row_first;
         if constexpr (F8) {
           load_tile8(-1, rr);
+        } else if (stream_kv) {
+          dma_region<DK / 8, 2>(kc, p.k_stride, buf, rr, w, lane);
+          if constexpr (!VA) dma_region<DV / 8, 2>(vc, p.v_stride, buf + C::VOFF, rr, w, lane);
         } else {
           dma_region<DK / 8>(kc, p.k_stride, buf, rr, w, lane);
           if constexpr (!VA) dma_region<DV / 8>(vc, p.v_stride, buf + C::VOFF, rr, w, lane);
