@@ -24,9 +24,9 @@
 //
 // 8-bit (E4M3) cache: the score waves load the next tile's codes into
 // registers before their products, then convert them to bf16 and write them
-// in the same ring slot layout, so the products read bf16 as above.  Each code is converted once per work-group; the cache bytes read
-// are halved.  The value waves, whose accumulators fill their registers, do
-// no staging.
+// in the same ring slot layout, so the products read bf16 as above.  Each
+// code is converted once per work-group; the cache bytes read are halved.
+// The value waves, whose accumulators fill their registers, do no staging.
 #include <type_traits>
 
 #include "e4m3.h"
@@ -55,19 +55,16 @@ constexpr float kLazy = 8.0f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
-// LDS swizzle (128 banks of 4 bytes; a 16-byte read is served 32 lanes at a
-// time, a transposing 8-byte read 64 lanes at a time).  Chunk c (16 bytes)
-// of row r of a region with CPR chunks per row sits at slot swz<CPR>(c, r):
-//   CPR >= 32: c ^ 2*(r mod 16) -- a key read (16 rows x 2 adjacent chunks)
-//              and a value transpose read (16 rows x one chunk pair) both
-//              cover 32 distinct slots of a 512-byte window;
-//   CPR == 8:  c ^ ((r / 2) mod 8) for 128-byte RoPE rows.
-template <int CPR>
-__device__ __forceinline__ int swz(int c, int r) {
-  static_assert(CPR == 8 || CPR == 32 || CPR == 64, "region row length");
-  if constexpr (CPR >= 32) return c ^ ((r & 15) << 1);
-  else return c ^ ((r >> 1) & 7);
-}
+// LDS layout of a tile (128 banks of 4 bytes; a 16-byte read is served 32
+// lanes at a time, a transposing 8-byte read 64 lanes at a time).
+//   Latent rows: a row stride of DK + 16 elements (32 bytes of padding), so
+//   row r starts 8 r banks on.  A key read (16 rows x 2 adjacent chunks) and
+//   a value transpose read (16 rows x 32 bytes) both cover 128 distinct
+//   banks, and the offsets of one lane's reads differ by constants that the
+//   instruction's offset field holds.
+//   RoPE rows (128 bytes, unpadded): chunk c of row r at slot c ^ ((r / 2)
+//   mod 8).
+__device__ __forceinline__ int swz_rope(int c, int r) { return c ^ ((r >> 1) & 7); }
 
 __device__ __forceinline__ s16x4 lds_read_tr(const bf16 *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
@@ -192,8 +189,9 @@ struct SCfg {
   static constexpr int KSN = DK / 32;         // of which on the latent
   static constexpr int MTV = DK / 64;         // value column tiles per value wave
   static constexpr int CPT = DK / 8;          // 16-byte chunks per latent row
-  static constexpr int ROFF = kT * DK;        // RoPE region of a tile buffer
-  static constexpr int BUF = kT * (DK + DR);  // elements per tile buffer
+  static constexpr int RS = DK + 16;          // latent row stride in LDS (elements)
+  static constexpr int ROFF = kT * RS;        // RoPE region of a tile buffer
+  static constexpr int BUF = kT * (RS + DR);  // elements per tile buffer
   // tile loads: every wave stages 4 latent rows (one instruction each); with
   // a RoPE key each score wave also stages 8 RoPE rows (one instruction when
   // the tile is on one page, eight otherwise; waiting for the count then
@@ -207,7 +205,7 @@ struct SCfg {
 template <int DK, int DR, bool F8>
 __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodeParams p) {
   using C = SCfg<DK, DR>;
-  constexpr int KS = C::KS, KSN = C::KSN, MTV = C::MTV, CPT = C::CPT, NLL = C::NLL;
+  constexpr int KS = C::KS, KSN = C::KSN, MTV = C::MTV, CPT = C::CPT, NLL = C::NLL, RS = C::RS;
   // tile ring as distinct LDS objects (loads into one are provably
   // independent of reads of the others)
   __shared__ __attribute__((aligned(16))) bf16 s_b0[C::BUF];
@@ -254,31 +252,28 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
     // columns 16 MTV vw ..
     const int sw = wu, vw = wu - 4;
 
-    // ---- per-lane LDS offsets (elements) of this role's fragment reads.
-    // The swizzle only flips bits 4..7 of an offset, so the offsets of one
-    // lane differ by an XOR with a constant:
-    //  score: key A operand (token block tt): row 16tt + n, chunk 4ks + g:
-    //         koff0 ^ 32 (ks mod 8), plus 256 (ks / 8);
+    // ---- per-lane LDS offsets (elements) of this role's fragment reads:
+    //  score: key A operand (token block tt): latent row 16tt + n, chunk
+    //         4ks + g at koff0 + 16 tt RS + 32 ks; RoPE chunk 4(ks - KSN) + g
+    //         at roff[(ks - KSN) mod 2] (swizzled);
     //  value: transpose read of column tile MTV vw + mt: lane (g, n) reads
     //         row 4g + n/4 (and the same 16 rows on) at columns 16 (MTV vw +
-    //         mt) + 4(n%4)..+3: voff0 ^ 16 mt.
+    //         mt) + 4(n%4)..+3: voff0 + 16 mt.
     int koff0 = 0, roff[2] = {0, 0}, voff0 = 0;
     if constexpr (kScore) {
-      koff0 = n * DK + swz<CPT>(g, n) * 8;
+      koff0 = n * RS + 8 * g;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) roff[e] = DR > 0 ? n * DR + swz<8>(4 * e + g, n) * 8 : 0;
+      for (int e = 0; e < 2; ++e) roff[e] = DR > 0 ? n * DR + swz_rope(4 * e + g, n) * 8 : 0;
     } else if constexpr (kValue) {
       const int rv = 4 * g + (n >> 2);
-      voff0 = rv * DK + swz<CPT>(2 * MTV * vw + ((n & 3) >> 1), rv) * 8 + 4 * (n & 1);
+      voff0 = rv * RS + 16 * MTV * vw + 4 * (n & 3);
     }
 
-    // tile loads: lane offsets of latent row 8e + wu (they depend on e mod
-    // 2) and, for a score wave, of RoPE rows 8 sw .. 8 sw + 7, relative to a
+    // tile loads: a latent row lands as it is (lane L: bytes 16 L .. of the
+    // row); a score wave's RoPE rows 8 sw .. 8 sw + 7: rofs, relative to the
     // tile's first row
-    int lofs[2], rofs = 0;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) lofs[e] = swz<CPT>(lane % CPT, kWaves * e + wu) * 16;
-    if constexpr (kScore && DR > 0) rofs = (int)((lane >> 3) * rstr) + swz<8>(lane & 7, 8 * sw + (lane >> 3)) * 16;
+    int rofs = 0;
+    if constexpr (kScore && DR > 0) rofs = (int)((lane >> 3) * rstr) + swz_rope(lane & 7, 8 * sw + (lane >> 3)) * 16;
 
     if constexpr (!F8) {
       // One empty-range load (no memory access) into each ring buffer in
@@ -398,7 +393,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
           for (int e = 0; e < NLL; ++e) {
             const int t = kWaves * e + wu;
             if (CPT == 64 || lane < CPT)
-              lds_dma16(rk, buf + t * DK, static_cast<unsigned>(lofs[e & 1]), static_cast<unsigned>(t * kstr));
+              lds_dma16(rk, buf + t * RS, static_cast<unsigned>(16 * lane), static_cast<unsigned>(t * kstr));
           }
           if constexpr (kScore && DR > 0)
             lds_dma16(make_rsrc(rcb + row0 * rstr, dma_range), buf + C::ROFF + 8 * sw * DR,
@@ -410,7 +405,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
           const int t = kWaves * e + wu;
           const long long row = __builtin_amdgcn_readlane(dma_rows, t);
           if (CPT == 64 || lane < CPT)
-            lds_dma16(make_rsrc(kcb + row * kstr, dma_range), buf + t * DK, static_cast<unsigned>(lofs[e & 1]), 0u);
+            lds_dma16(make_rsrc(kcb + row * kstr, dma_range), buf + t * RS, static_cast<unsigned>(16 * lane), 0u);
         }
         if constexpr (kScore && DR > 0) {
           // one instruction (8 lanes) per row
@@ -420,7 +415,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
             const long long row = __builtin_amdgcn_readlane(dma_rows, t);
             if (lane < 8)
               lds_dma16(make_rsrc(rcb + row * rstr, dma_range), buf + C::ROFF + t * DR,
-                        static_cast<unsigned>(swz<8>(lane, t) * 16), 0u);
+                        static_cast<unsigned>(swz_rope(lane, t) * 16), 0u);
           }
         }
       };
@@ -465,16 +460,16 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
 #pragma unroll
         for (int i = 0; i < NPL; ++i) {
           const int q = lane + 64 * i, t = 4 * (q / PPR) + sw, c16 = q % PPR;
-          bf16 *row = buf + t * DK;
-          *reinterpret_cast<u32x4 *>(row + swz<CPT>(2 * c16, t) * 8) = e4m3x8_to_bf16x8_bits(stg[S][i][0], stg[S][i][1]);
-          *reinterpret_cast<u32x4 *>(row + swz<CPT>(2 * c16 + 1, t) * 8) = e4m3x8_to_bf16x8_bits(stg[S][i][2], stg[S][i][3]);
+          bf16 *row = buf + t * RS + 16 * c16;
+          *reinterpret_cast<u32x4 *>(row) = e4m3x8_to_bf16x8_bits(stg[S][i][0], stg[S][i][1]);
+          *reinterpret_cast<u32x4 *>(row + 8) = e4m3x8_to_bf16x8_bits(stg[S][i][2], stg[S][i][3]);
         }
         if constexpr (kRopeStage) {
           if (lane < 32) {
             const int t = 8 * sw + (lane >> 2), c16 = lane & 3;
             bf16 *row = buf + C::ROFF + t * DR;
-            *reinterpret_cast<u32x4 *>(row + swz<8>(2 * c16, t) * 8) = e4m3x8_to_bf16x8_bits(stg[S][NPL][0], stg[S][NPL][1]);
-            *reinterpret_cast<u32x4 *>(row + swz<8>(2 * c16 + 1, t) * 8) = e4m3x8_to_bf16x8_bits(stg[S][NPL][2], stg[S][NPL][3]);
+            *reinterpret_cast<u32x4 *>(row + swz_rope(2 * c16, t) * 8) = e4m3x8_to_bf16x8_bits(stg[S][NPL][0], stg[S][NPL][1]);
+            *reinterpret_cast<u32x4 *>(row + swz_rope(2 * c16 + 1, t) * 8) = e4m3x8_to_bf16x8_bits(stg[S][NPL][2], stg[S][NPL][3]);
           }
         }
       };
@@ -495,7 +490,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
         auto kload = [&](int ks, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
-            const bf16 *src = ks < KSN ? ht + 16 * tt * DK + (ko0 ^ (32 * (ks & 7))) + 256 * (ks >> 3)
+            const bf16 *src = ks < KSN ? ht + 16 * tt * RS + ko0 + 32 * ks
                                        : ht + C::ROFF + 16 * tt * DR + ro[(ks - KSN) & 1];
             dst[tt] = *reinterpret_cast<const bf16x8 *>(src);
           }
@@ -580,8 +575,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const DecodePara
         constexpr int VD = 3;
         bf16x8 va[VD + 1];
         auto vload = [&](int mt) __attribute__((always_inline)) {
-          const bf16 *lo = ht + (vo0 ^ (16 * mt));
-          return join(lds_read_tr(lo), lds_read_tr(lo + 16 * DK));
+          const bf16 *lo = ht + vo0 + 16 * mt;
+          return join(lds_read_tr(lo), lds_read_tr(lo + 16 * RS));
         };
 #pragma unroll
         for (int mt = 0; mt < VD && mt < MTV; ++mt) va[mt] = vload(mt);
