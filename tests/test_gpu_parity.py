@@ -1017,6 +1017,59 @@ def test_constant_value_rows_give_that_value(lkv, kind, h_q, splits):
         float(np.max(np.abs(got - want) / (np.abs(want) + 1e-30)))
 
 
+def _scale_keys_along_sequence(x, w, kind, direction):
+    """Multiply a key-only part of cached token j of every sequence by a
+    factor that grows along the sequence (or shrinks, falling), rounded back
+    to bf16, leaving the values as they are.  MLA: the shared RoPE key, by 1
+    to 32 (the latent is also the value); GQA: the key rows, by 1 to 8."""
+    top = 32.0 if kind == "mla" else 8.0
+    for b in range(w.B):
+        L = int(x["seqlens"][b])
+        if L == 0:
+            continue
+        j = np.arange(L)
+        f = 1.0 + (top - 1.0) * j / max(L - 1, 1)
+        if direction == "fall":
+            f = f[::-1]
+        pages = x["block_table"][b, j // w.page_size]
+        slots = j % w.page_size
+        if kind == "mla":
+            c0 = w.n_lat * w.d_c
+            rows = li.bf16_bits_to_f32(x["kv"][pages, slots, c0:])
+            x["kv"][pages, slots, c0:] = li.to_bf16_bits(rows * f[:, None])
+        else:
+            rows = li.bf16_bits_to_f32(x["k_cache"][pages, slots])
+            x["k_cache"][pages, slots] = li.to_bf16_bits(rows * f[:, None, None])
+
+
+@pytest.mark.parametrize("kind,h_q,splits,direction", [
+    ("mla", 128, 0, "rise"), ("mla", 128, 5, "rise"), ("mla", 128, 0, "fall"),
+    ("mla", 16, 0, "rise"), ("mla", 16, 3, "fall"), ("gqa", 32, 0, "rise"), ("gqa", 32, 4, "fall")])
+def test_running_maximum_moves_along_the_cache(lkv, oracle, kind, h_q, splits, direction):
+    """Scores whose spread grows (or shrinks) many times over along each
+    sequence, so that the lazy reference maximum moves several times in the middle of a
+    share (rising) or is set early and later tiles are small (falling), with
+    random values: the output and LSE must still meet the oracle, which
+    catches a wrong rescale factor (not only a missing one)."""
+    seqlens = (700, 1500, 64)
+    if kind == "mla":
+        w, x = small_mla(1400 + h_q + splits + (1 if direction == "fall" else 0), h_q=h_q,
+                         seqlens=seqlens)
+    else:
+        w, x = _gqa_small(1450 + splits + (1 if direction == "fall" else 0), h_q=h_q, n_kv=8,
+                          seqlens=seqlens)
+    _scale_keys_along_sequence(x, w, kind, direction)
+    note(f"case running maximum {kind} h_q={h_q} splits={splits} {direction}")
+    if kind == "mla":
+        out, lse = run_mla(lkv, w, mla_device_inputs(x, w, torch), x=x, num_splits=splits)
+        ro, rl = oracle_mla(oracle, w, x)
+    else:
+        out, lse = _run_gqa(lkv, w, x, num_splits=splits)
+        ro, rl = _oracle_gqa(oracle, w, x)
+    assert_close(from_dev(out), ro, from_dev(lse), rl,
+                 what=f"running maximum {kind} h_q={h_q} splits={splits} {direction}")
+
+
 # ------------------------------------------------------------------ limits
 def test_mla_max_query_tokens(lkv, oracle):
     """s_q = 64, the largest the ABI takes: 1024 query rows on one latent head
