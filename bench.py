@@ -403,6 +403,25 @@ def setup_gqla(w, x, args, torch, lkv, rf):
     torch.cuda.synchronize()
     t_exp8 = e0.elapsed_time(e1) * 1e-3 / n_exp
     del k8, v8
+    # context for the expansion (not part of the path): the vendor library's
+    # GEMM (torch.matmul, hipBLASLt) on the same product with contiguous
+    # operands -- no gather through the block table, one output matrix --
+    # timed the same way
+    n_ctx = int(np.sum(x["seqlens"]))
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    a_ctx = torch.randn((n_ctx, w.d_c), device="cuda", generator=gen).to(torch.bfloat16)
+    w_ctx = torch.randn((2 * w.n_kv * w.d_h, w.d_c), device="cuda", generator=gen).to(torch.bfloat16)
+    o_ctx = torch.empty((n_ctx, 2 * w.n_kv * w.d_h), dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):
+        torch.matmul(a_ctx, w_ctx.t(), out=o_ctx)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n_exp):
+        torch.matmul(a_ctx, w_ctx.t(), out=o_ctx)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_gemm = e0.elapsed_time(e1) * 1e-3 / n_exp
+    del a_ctx, w_ctx, o_ctx
     ks, vs = [k0], [v0]
     for _ in range(ROTATE - 1):
         ks.append(k0.clone())
@@ -506,6 +525,9 @@ def setup_gqla(w, x, args, torch, lkv, rf):
                                 "GB_per_s": ew8.bytes / t_exp8 / 1e9,
                                 "TFLOP_per_s": ew8.flops / t_exp8 / 1e12,
                                 "note": "the same expansion written as 8-bit E4M3 caches"},
+             "expansion_vendor_gemm": {"us": t_gemm * 1e6, "TFLOP_per_s": ew.flops / t_gemm / 1e12,
+                                       "note": "context only: torch.matmul (hipBLASLt) on contiguous "
+                                               "operands of the same product, no gather or scatter"},
              "absorb_query": {"us": t_abs, "flops": proj_flops, "bytes": proj_bytes,
                               "GB_per_s": proj_bytes / t_abs / 1e3,
                               "TFLOP_per_s": proj_flops / t_abs / 1e6},
