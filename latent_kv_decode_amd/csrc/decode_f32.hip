@@ -40,17 +40,42 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Tokens per tile for a row layout of `width` floats (key + RoPE key +
+// Tile geometry for a row layout of `width` floats (key + RoPE key +
 // separate value) after the query's dq floats: the LDS holds the query and,
-// per wave, T padded rows of width + 1 floats.
-__host__ __device__ inline int f32_tile_tokens(int width, int dq) {
+// per wave, a region of T token rows of `pitch` floats.
+//   4-byte staging: pitch = width + 1 (odd: a lane-per-token read of one
+//   column hits 64 different banks).
+//   16-byte staging (every row segment a whole number of 16-byte chunks):
+//   pitch = 4 CPR floats with CPR, the chunks per row, made odd, so that the
+//   16-byte reads of 16 consecutive token rows cover distinct banks; the
+//   region is rounded up to whole 64-chunk load instructions.
+struct F32Tile {
+  int T, pitch, region;  // tokens, floats per row, floats per wave region
+};
+__host__ __device__ inline F32Tile f32_tile(int width, int dq, bool v16) {
   const int avail = (kLdsBytes / 4 - dq) / kWaves;
-  const int t = avail / (width + 1);
-  return t < 1 ? 1 : (t > 64 ? 64 : t);
+  F32Tile t;
+  if (!v16) {
+    t.pitch = width + 1;
+    t.T = avail / t.pitch;
+    t.T = t.T < 1 ? 1 : (t.T > 64 ? 64 : t.T);
+    t.region = t.T * t.pitch;
+    return t;
+  }
+  const int cpr = (width / 4) | 1;
+  t.pitch = 4 * cpr;
+  t.T = 64;
+  while (t.T > 1 && 4 * ((t.T * cpr + 63) / 64 * 64) > avail) --t.T;
+  t.region = 4 * ((t.T * cpr + 63) / 64 * 64);
+  return t;
 }
 
 // rows_per_xcd: rows handled on one XCD, a multiple of the rows of one
 // sequence; work-group i runs row (i mod 8) * rows_per_xcd + i / 8.
+// V16: every row segment starts 16-byte aligned and is a whole number of
+// 16-byte chunks (the host checks pointers, strides and widths), so a tile is
+// gathered with 16-byte direct-to-LDS loads, 64 chunks per instruction.
+template <bool V16>
 __global__ void __launch_bounds__(64 * kWaves) f32_decode_kernel(const DecodeParams p, long long rows_per_xcd) {
   extern __shared__ float lds[];
   __shared__ float s_ml[2 * kWaves];
@@ -66,10 +91,10 @@ __global__ void __launch_bounds__(64 * kWaves) f32_decode_kernel(const DecodePar
   const bool v_alias = p.v == p.k && p.v_stride == p.k_stride && p.dv == p.dk;
   const int dq = p.dk + p.dr;                  // query (and key) width
   const int width = dq + (v_alias ? 0 : p.dv);  // floats per staged token row
-  const int T = f32_tile_tokens(width, dq);
-  const int pitch = width + 1;
+  const F32Tile geo = f32_tile(width, dq, V16);
+  const int T = geo.T, pitch = geo.pitch;
   float *q_l = lds;                             // [dq]
-  float *tile = lds + dq + wv * T * pitch;      // this wave's [T][pitch]
+  float *tile = lds + dq + wv * geo.region;     // this wave's [T][pitch]
   const float *q = static_cast<const float *>(p.q) + row * p.dk;
   const float *qr = p.dr ? static_cast<const float *>(p.q_rope) + row * p.dr : nullptr;
   const float *kc = static_cast<const float *>(p.k) + (long long)kvh * p.dk;
@@ -113,15 +138,45 @@ __global__ void __launch_bounds__(64 * kWaves) f32_decode_kernel(const DecodePar
             __builtin_amdgcn_global_load_lds(src + c0, (__attribute__((address_space(3))) void *)(dst + c0), 4, 0, 0);
       }
     };
-    stage(kc, p.k_stride, p.dk, 0);
-    if (p.dr) stage(rc, p.r_stride, p.dr, p.dk);
-    if (!v_alias) stage(vc, p.v_stride, p.dv, dq);
+    if constexpr (V16) {
+      // chunk q = 64 u + lane: 16 bytes of token q / CPR's row, chunk q mod
+      // CPR (key, then RoPE key, then separate value; the odd padding chunk
+      // and the chunks past the tile's tokens read a valid chunk that is
+      // never used)
+      const int cpr = pitch / 4, ck = p.dk / 4, cq = dq / 4, cw = width / 4;
+      const int nq = cnt * cpr;
+      for (int u = 0; 64 * u < nq; ++u) {
+        const int q = 64 * u + lane;
+        const int tok = min(q / cpr, cnt - 1), c = q % cpr;
+        const long long r = __shfl(crow, tok);
+        const float *src = kc + r * p.k_stride;
+        if (q < nq) {
+          if (c < ck) src += 4 * c;
+          else if (c < cq) src = rc + r * p.r_stride + 4 * (c - ck);
+          else if (c < cw) src = vc + r * p.v_stride + 4 * (c - cq);
+        }
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(tile + 256 * u), 16, 0, 0);
+      }
+    } else {
+      stage(kc, p.k_stride, p.dk, 0);
+      if (p.dr) stage(rc, p.r_stride, p.dr, p.dk);
+      if (!v_alias) stage(vc, p.v_stride, p.dv, dq);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     float s = -__builtin_inff();
     if (lane < cnt) {
       const float *kr = tile + lane * pitch;
       float dot = 0.f;
-      for (int d = 0; d < dq; ++d) dot += q_l[d] * kr[d];
+      if constexpr (V16) {
+        // four independent partial sums over 16-byte reads
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        f4 acc4 = {0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < dq / 4; ++c)
+          acc4 += *reinterpret_cast<const f4 *>(q_l + 4 * c) * *reinterpret_cast<const f4 *>(kr + 4 * c);
+        dot = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+      } else {
+        for (int d = 0; d < dq; ++d) dot += q_l[d] * kr[d];
+      }
       s = dot * p.scale_log2;
     }
     const float mnew = fmaxf(m, wave_max(s));
@@ -143,6 +198,17 @@ __global__ void __launch_bounds__(64 * kWaves) f32_decode_kernel(const DecodePar
         const float keep = d < p.dv ? 1.f : 0.f;
         float acc = 0.f;
         int jj = 0;
+        if constexpr (V16) {
+          // four independent partial sums
+          float a1 = 0.f, a2 = 0.f, a3 = 0.f;
+          for (; jj + 4 <= cnt; jj += 4) {
+            acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), jj + 0)) * vt[(jj + 0) * pitch + dc];
+            a1 += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), jj + 1)) * vt[(jj + 1) * pitch + dc];
+            a2 += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), jj + 2)) * vt[(jj + 2) * pitch + dc];
+            a3 += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), jj + 3)) * vt[(jj + 3) * pitch + dc];
+          }
+          acc = (acc + a1) + (a2 + a3);
+        }
         for (; jj + 4 <= cnt; jj += 4) {
           const float v0 = vt[(jj + 0) * pitch + dc], v1 = vt[(jj + 1) * pitch + dc];
           const float v2 = vt[(jj + 2) * pitch + dc], v3 = vt[(jj + 3) * pitch + dc];
@@ -205,16 +271,28 @@ hipError_t launch_f32_decode(const DecodeParams &p, hipStream_t s, const LaunchE
   const bool v_alias = p.v == p.k && p.v_stride == p.k_stride && p.dv == p.dk;
   const int dq = p.dk + p.dr;
   const int width = dq + (v_alias ? 0 : p.dv);
-  const int T = f32_tile_tokens(width, dq);
+  // 16-byte staging when every row segment starts 16-byte aligned and is a
+  // whole number of 16-byte chunks
+  auto al16 = [](const void *x) { return x == nullptr || (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
+  const bool v16 = al16(p.k) && p.dk % 4 == 0 && p.k_stride % 4 == 0 &&
+                   (p.dr == 0 || (al16(p.r) && p.dr % 4 == 0 && p.r_stride % 4 == 0)) &&
+                   (v_alias || (al16(p.v) && p.dv % 4 == 0 && p.v_stride % 4 == 0));
+  const F32Tile geo = f32_tile(width, dq, v16);
   // the tiles, and after them the merge area [kWaves][dv], fit the LDS
-  const size_t lds = (size_t)(dq + kWaves * T * (width + 1)) * sizeof(float);
-  if (lds > (size_t)kLdsBytes || (size_t)kWaves * p.dv > (size_t)kWaves * T * (width + 1))
+  const size_t lds = (size_t)(dq + kWaves * geo.region) * sizeof(float);
+  if (lds > (size_t)kLdsBytes || (size_t)kWaves * p.dv > (size_t)kWaves * geo.region ||
+      (size_t)geo.T * geo.pitch > (size_t)geo.region)
     return hipErrorInvalidValue;
-  if (ev.start || ev.stop)
-    hipExtLaunchKernelGGL(f32_decode_kernel, dim3((unsigned)grid), dim3(64 * kWaves), lds, s, ev.start, ev.stop, 0,
-                          p, per_xcd);
+  auto go = [&](auto kern) {
+    if (ev.start || ev.stop)
+      hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * kWaves), lds, s, ev.start, ev.stop, 0, p, per_xcd);
+    else
+      hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * kWaves), lds, s, p, per_xcd);
+  };
+  if (v16)
+    go(f32_decode_kernel<true>);
   else
-    hipLaunchKernelGGL(f32_decode_kernel, dim3((unsigned)grid), dim3(64 * kWaves), lds, s, p, per_xcd);
+    go(f32_decode_kernel<false>);
   return hipGetLastError();
 }
 

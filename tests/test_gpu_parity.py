@@ -60,6 +60,20 @@ def test_fp32_variants(lkv, oracle, s_q, causal, n_lat):
     assert_close(from_dev(out), ro, from_dev(lse), rl, f32=True, what="fp32")
 
 
+@pytest.mark.parametrize("d_c,d_rope", [(64, 6), (62, 16), (30, 4)])
+def test_fp32_rows_not_16_byte_chunks(lkv, oracle, d_c, d_rope):
+    """Token rows whose segments are not whole 16-byte chunks (a RoPE width
+    of 6, a latent width of 62 or 30 floats): the float32 kernel stages them
+    with 4-byte loads instead of 16-byte ones."""
+    w, x = small_mla(150 + d_c + d_rope, B=3, h_q=16, s_q=1, d_c=d_c, d_rope=d_rope, page=16,
+                     seqlens=[1, 130, 257], dtype="f32")
+    note(f"case fp32 rows d_c={d_c} d_rope={d_rope}")
+    d = mla_device_inputs(x, w, torch)
+    out, lse = run_mla(lkv, w, d)
+    ro, rl = oracle_mla(oracle, w, x)
+    assert_close(from_dev(out), ro, from_dev(lse), rl, f32=True, what="fp32 rows")
+
+
 # ------------------------------------------------------------------ bf16 MLA
 @pytest.mark.parametrize("s_q,causal,splits", [
     (1, True, 0), (1, True, 1), (1, True, 2), (1, True, 7), (1, True, 1000),
