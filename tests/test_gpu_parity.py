@@ -1084,6 +1084,63 @@ def test_running_maximum_moves_along_the_cache(lkv, oracle, kind, h_q, splits, d
                  what=f"running maximum {kind} h_q={h_q} splits={splits} {direction}")
 
 
+# ---------------------------------------------------- LKV_DEBUG_CHECKS=1
+_DEBUG_CHILD = r"""
+import math, sys
+import torch
+import latent_kv_decode_amd as lkv
+import lkv_inputs as li
+from tests.gpu_common import mla_device_inputs, run_mla
+lkv.load_library()
+w = li.Workload(name="dbg", kind="mla", dtype="bf16", B=3, h_q=128, s_q=1, page_size=64, n_lat=1,
+                d_c=512, d_rope=64, seqlens=(100, 300, 65), table="shuffled", causal=True,
+                max_pages=None, scale=1 / math.sqrt(576), seed=31)
+x = li.generate(w)
+d = mla_device_inputs(x, w, torch)
+npg = int(x["num_pages"])
+run_mla(lkv, w, d, num_pages=npg)
+torch.cuda.synchronize()
+print("good call ok", flush=True)
+# every page of the pool is used, so a pool one page smaller leaves one
+# table entry outside it (that page exists in memory)
+try:
+    run_mla(lkv, w, d, num_pages=npg - 1)
+    print("bad page accepted", flush=True)
+except lkv.LkvError as e:
+    print("bad page rejected", e.status, flush=True)
+# a length past max_pages * page_size in the first sequence (the row after
+# it in the table holds valid pages)
+sl = d["seqlens"].clone()
+sl[0] = x["block_table"].shape[1] * w.page_size + 1
+try:
+    run_mla(lkv, w, dict(d, seqlens=sl), num_pages=npg)
+    print("bad length accepted", flush=True)
+except lkv.LkvError as e:
+    print("bad length rejected", e.status, flush=True)
+"""
+
+
+def test_debug_checks_read_back_the_device_contract():
+    """LKV_DEBUG_CHECKS=1 (read once per process, so the calls run in a child
+    process): with no host copies given, the library reads the lengths and
+    the block table back from the device and rejects a table entry outside
+    the pool and a length past max_pages * page_size before any launch
+    (LKV_ERR_SHAPE = 2); a valid call still runs."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, LKV_DEBUG_CHECKS="1", PYTHONPATH=root)
+    note("case LKV_DEBUG_CHECKS=1 child process")
+    r = subprocess.run([sys.executable, "-c", _DEBUG_CHILD], env=env, cwd=root, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    lines = r.stdout.splitlines()
+    assert "good call ok" in lines, r.stdout
+    assert "bad page rejected 2" in lines, r.stdout
+    assert "bad length rejected 2" in lines, r.stdout
+
+
 # ------------------------------------------------------------------ limits
 def test_mla_max_query_tokens(lkv, oracle):
     """s_q = 64, the largest the ABI takes: 1024 query rows on one latent head
