@@ -274,15 +274,20 @@ hipError_t launch_f32_decode(const DecodeParams &p, hipStream_t s, const LaunchE
   // 16-byte staging when every row segment starts 16-byte aligned and is a
   // whole number of 16-byte chunks
   auto al16 = [](const void *x) { return x == nullptr || (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
-  const bool v16 = al16(p.k) && p.dk % 4 == 0 && p.k_stride % 4 == 0 &&
-                   (p.dr == 0 || (al16(p.r) && p.dr % 4 == 0 && p.r_stride % 4 == 0)) &&
-                   (v_alias || (al16(p.v) && p.dv % 4 == 0 && p.v_stride % 4 == 0));
-  const F32Tile geo = f32_tile(width, dq, v16);
   // the tiles, and after them the merge area [kWaves][dv], fit the LDS
+  auto fits = [&](const F32Tile &g) {
+    return (size_t)(dq + kWaves * g.region) * sizeof(float) <= (size_t)kLdsBytes && p.dv <= g.region &&
+           g.T * g.pitch <= g.region;
+  };
+  bool v16 = al16(p.k) && p.dk % 4 == 0 && p.k_stride % 4 == 0 &&
+             (p.dr == 0 || (al16(p.r) && p.dr % 4 == 0 && p.r_stride % 4 == 0)) &&
+             (v_alias || (al16(p.v) && p.dv % 4 == 0 && p.v_stride % 4 == 0));
+  // rows so wide that the 16-byte layout's padding overflows the LDS take
+  // the 4-byte path
+  if (v16 && !fits(f32_tile(width, dq, true))) v16 = false;
+  const F32Tile geo = f32_tile(width, dq, v16);
+  if (!fits(geo)) return hipErrorInvalidValue;
   const size_t lds = (size_t)(dq + kWaves * geo.region) * sizeof(float);
-  if (lds > (size_t)kLdsBytes || (size_t)kWaves * p.dv > (size_t)kWaves * geo.region ||
-      (size_t)geo.T * geo.pitch > (size_t)geo.region)
-    return hipErrorInvalidValue;
   auto go = [&](auto kern) {
     if (ev.start || ev.stop)
       hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * kWaves), lds, s, ev.start, ev.stop, 0, p, per_xcd);
